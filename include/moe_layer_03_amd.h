@@ -1,0 +1,210 @@
+/*
+ * moe_layer_03_amd -- one expert-parallel rank's share of a Mixture-of-Experts
+ * layer on AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The operation is the one "Hosting Qwen on Blackwell" (Perplexity) states
+ * for its prefill expert-parallel kernel (section "Expert Parallel") and its
+ * dispatch/combine pair (section "MoE Dispatch - Combine"): every rank holds
+ * all T tokens; the router sends each token to K of E experts (128 experts,
+ * 8 per token in section "Pre-remplisseurs"); the rank selects the tokens
+ * routed to its own experts [e_begin, e_end), packs them into per-expert
+ * contiguous buffers, runs one GEMM problem per local expert (section
+ * "MoE GEMM"), and accumulates the weighted expert outputs back in token
+ * order.  That local sum is the rank's partial output; adding the partial
+ * outputs of all ranks (an all-reduce) is outside this library.
+ *
+ * Readings of what the pages leave open (the router function, the expert
+ * activation, orders, precision) are fixed here and stated per call.
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers (HIP device memory), row-major,
+ *     owned by the caller, 16-byte aligned.  The library never allocates
+ *     or frees memory and keeps no global state besides a per-thread copy
+ *     of the last HIP error code.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ *     A call only enqueues work on it and returns; outputs are valid once
+ *     the stream has synchronised, and inputs must stay alive until then.
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     call returns an error status and enqueues nothing.
+ *   - Non-finite inputs (NaN, Inf) are outside the contract.
+ *   - bf16 tensors are raw bfloat16 bit patterns in uint16_t storage.
+ */
+#ifndef MOE_LAYER_03_AMD_H
+#define MOE_LAYER_03_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG (-1)   /* bad shape, range, null or misaligned pointer */
+#define MOE_ERR_UNSUPPORTED (-2)   /* valid but not implemented (dtype mix, H or I not a multiple of 64, K > 64) */
+#define MOE_ERR_WORKSPACE   (-3)   /* ws_bytes smaller than the matching *_workspace_bytes() */
+#define MOE_ERR_HIP         (-4)   /* a HIP launch failed; see moe_last_hip_error() */
+
+/* Element types.  MOE_F16 appears only for intermediates and GEMM outputs. */
+#define MOE_F32  0
+#define MOE_BF16 1
+#define MOE_F16  2
+
+/* Grouped-GEMM operand selector and epilogues. */
+#define MOE_GEMM_GATE_UP 0   /* A = packed tokens [*, H], B = gate and up weights of each expert  */
+#define MOE_GEMM_DOWN    1   /* A = SwiGLU activations [*, I], B = down weights of each expert    */
+#define MOE_EPI_NONE     0   /* C = A.B (gate/up: columns 0..I-1 gate, I..2I-1 up)                 */
+#define MOE_EPI_SWIGLU   1   /* C = silu(A.Wg) * (A.Wu), silu(z) = z / (1 + exp(-z)); gate/up only */
+
+/*
+ * Problem shape of one rank.
+ *   T tokens, H hidden size, E experts in the layer, K experts per token,
+ *   I expert intermediate size, local experts [e_begin, e_end).
+ * Limits: T >= 0 (T == 0 makes every call a no-op), 1 <= K <= E <= 1024,
+ * K <= 64, 0 <= e_begin < e_end <= E, H >= 64 and I >= 64 and both
+ * multiples of 64, T * K < 2^31.
+ * E_loc = e_end - e_begin.  cap = T * min(K, E_loc) bounds the number of
+ * (token, slot) pairs that can be routed to local experts; buffers indexed by
+ * packed row are sized by cap, and only the first N_loc = offsets[E_loc]
+ * rows are meaningful.
+ */
+typedef struct moe_shape {
+    int32_t T, H, E, K, I, e_begin, e_end;
+} moe_shape;
+
+/* Bytes of scratch memory moe_dispatch() needs (host-only, no HIP call). */
+size_t moe_dispatch_workspace_bytes(const moe_shape* s);
+
+/* Bytes of scratch memory moe_layer() needs (host-only, no HIP call). */
+size_t moe_layer_workspace_bytes(const moe_shape* s);
+
+/* Bytes of the packed expert weights of the E_loc local experts (host-only). */
+size_t moe_packed_weight_bytes(const moe_shape* s);
+
+/*
+ * moe_pack_weights -- static conversion of the local experts' weights into
+ * the layout the grouped GEMM streams (the pages convert their weights
+ * statically once, section "Quantification").  Run once, outside any timed
+ * region.
+ *   w_gate [E_loc, H, I], w_up [E_loc, H, I], w_down [E_loc, I, H]: the
+ *   expert FFN is y = (silu(x Wg) * (x Wu)) Wd; dtype MOE_BF16 or MOE_F32.
+ *   Gate and up weights keep bf16 (bf16 input) or are rounded to fp16
+ *   (float32 input); down weights are converted to fp16 (exact for bf16
+ *   values of magnitude 2^-17 .. 65504; fp16 conversions saturate at 65504).
+ *   packed: moe_packed_weight_bytes(s) bytes, written; opaque layout.
+ */
+int moe_pack_weights(const moe_shape* s, const void* w_gate, const void* w_up, const void* w_down,
+                     int dtype, void* packed, void* stream);
+
+/*
+ * moe_route -- router logits, softmax over the E experts, top-K, renormalised
+ * ("Pre-remplisseurs": each token is routed to 8 of the 128 experts; the pages
+ * do not name the router function, this library takes softmax -> top-K ->
+ * renormalise).
+ *   x [T, H], w_router [H, E]: both MOE_F32 or both MOE_BF16.
+ *   bias [E] float32 or NULL: added to each logit after the dot product.
+ *   logits (output, optional) [T, E] float32:
+ *       l[t,e] = fma-chain over h = 0..H-1 ascending, starting from +0.0f,
+ *       acc = fmaf(x[t,h], w_router[h,e], acc); then acc + bias[e].
+ *       This order is part of the definition: it decides near-ties.
+ *   topk_idx (output) [T, K] int32: the K largest logits, slot 0 the largest,
+ *       equal logits (-0 == +0) ordered by ascending expert index.
+ *   topk_w (output) [T, K] float32: exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ *       over the chosen K, i.e. the softmax probabilities renormalised.
+ */
+int moe_route(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
+              const float* bias, int32_t* topk_idx, float* topk_w, float* logits, void* stream);
+
+/*
+ * moe_route_from_logits -- the selection and weighting step of moe_route on
+ * caller-supplied logits [T, E] float32 (same outputs, same rules).
+ */
+int moe_route_from_logits(const moe_shape* s, const float* logits, int32_t* topk_idx, float* topk_w,
+                          void* stream);
+
+/*
+ * moe_dispatch -- select the (token, slot) pairs routed to local experts and
+ * pack the tokens per expert ("Expert Parallel": the inputs are replicated on
+ * every rank, so dispatch only selects the tokens routed to the rank's
+ * experts, aggregates the routing information and prepares the GEMM input
+ * buffers).
+ *   topk_idx [T, K] int32 (from moe_route).
+ *   counts (output) [E_loc] int32: pairs routed to expert e_begin + i.
+ *   offsets (output) [E_loc + 1] int32: exclusive prefix sum of counts.
+ *   row_token, row_slot (output) [cap] int32: token and slot of packed row r;
+ *       an expert's rows are in ascending token order, experts ascending.
+ *   slot_row (output) [T, K] int32: packed row of (t, j), -1 if not local.
+ *   x [T, H] (MOE_F32 or MOE_BF16) and x_packed (output) [cap, H]:
+ *       x_packed[r] = x[row_token[r]] in the GEMM operand type -- a bf16 copy
+ *       of bf16 x, fp16 (nearest-even, saturating) for float32 x; both NULL
+ *       to skip the pack.
+ *   ws: moe_dispatch_workspace_bytes(s) bytes of device scratch.
+ */
+int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int x_dtype,
+                 int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_slot,
+                 int32_t* slot_row, uint16_t* x_packed, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_gemm -- one GEMM problem per local expert over its packed rows
+ * ("MoE GEMM"); rows [offsets[i], offsets[i+1]) use expert e_begin + i.
+ *   which = MOE_GEMM_GATE_UP: a [cap, H] = x_packed, a_dtype MOE_BF16 for
+ *       weights packed from bf16, MOE_F16 for weights packed from float32;
+ *       epilogue MOE_EPI_SWIGLU -> c [cap, I], or MOE_EPI_NONE -> c [cap, 2I]
+ *       (gate columns then up columns).
+ *   which = MOE_GEMM_DOWN: a [cap, I] fp16 (a_dtype MOE_F16); epilogue
+ *       MOE_EPI_NONE -> c [cap, H].
+ *   c_dtype MOE_F32, MOE_BF16 or MOE_F16 (16-bit outputs round to nearest
+ *   even; fp16 saturates at 65504); products accumulate in float32.  Rows
+ *   >= N_loc are not written.
+ *   packed: the buffer moe_pack_weights() wrote for the same shape.
+ *   offsets [E_loc + 1] int32, on the device (counts never visit the host).
+ */
+int moe_grouped_gemm(const moe_shape* s, const uint16_t* a, int a_dtype, const int32_t* offsets, const void* packed,
+                     int which, int epilogue, void* c, int c_dtype, void* stream);
+
+/*
+ * moe_combine -- weighted local accumulation back to token order
+ * ("MoE Dispatch - Combine", "Expert Parallel": the combine kernel first
+ * accumulates the contributions of the experts on the current rank).
+ *   out[t, :] = sum over j = 0..K-1 ascending with slot_row[t,j] >= 0 of
+ *               topk_w[t,j] * y_packed[slot_row[t,j], :], in float32.
+ *   Rows of tokens with no local expert are written as zeros.
+ *   y_packed [cap, H], y_dtype MOE_F16, MOE_BF16 or MOE_F32; slot_row [T, K] int32,
+ *   topk_w [T, K] float32,
+ *   out (output) [T, H] float32, fully overwritten.
+ */
+int moe_combine(const moe_shape* s, const void* y_packed, int y_dtype, const int32_t* slot_row, const float* topk_w,
+                float* out, void* stream);
+
+/*
+ * moe_layer -- route, dispatch, grouped gate/up GEMM with the SwiGLU epilogue,
+ * grouped down GEMM and combine, enqueued on one stream with no host
+ * synchronisation (the pages split the prefill kernel into several kernels
+ * and fuse the decode kernel into one, section "Expert Parallel").
+ *   x [T, H], w_router [H, E] as in moe_route; bias [E] or NULL;
+ *   packed: moe_pack_weights() output; out (output) [T, H] float32.
+ *   topk_idx, topk_w, counts, offsets, row_token, row_slot, slot_row:
+ *       optional outputs (NULL: kept in the workspace), as in moe_route and
+ *       moe_dispatch.
+ *   ws: moe_layer_workspace_bytes(s) bytes of device scratch.
+ *   x and the packed weights must come from the same dtype.  Intermediates:
+ *   packed tokens in the gate/up operand type (bf16, or fp16 for float32
+ *   layers); SwiGLU activations and expert outputs in fp16.
+ */
+int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
+              const float* bias, const void* packed, float* out,
+              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+              int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* hipError_t value of the last MOE_ERR_HIP returned on the calling thread (0 if none). */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LAYER_03_AMD_H */

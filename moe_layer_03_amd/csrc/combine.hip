@@ -1,0 +1,85 @@
+// Combine: weighted local accumulation back into token order.
+//
+// "Hosting Qwen on Blackwell" (Perplexity), sections "MoE Dispatch - Combine"
+// and "Expert Parallel": combine accumulates, with the routing weights, the
+// outputs of the experts held by the current rank for every token (the
+// cross-rank all-reduce that follows is outside this library).
+//
+// Gather form: the workgroup that owns token t reads its slot_row/topk_w
+// entries (at most K rows), adds w * y_row in ascending slot order in float32
+// and writes the whole output row once -- no atomics, deterministic.  Each
+// thread handles 8 consecutive features: one 16-byte bf16/fp16 load (or two
+// 16-byte float32 loads) per slot, two 16-byte float32 stores.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokensPerBlock = 2;
+
+template <typename YT, bool F16>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict__ y, int T, int H, int K,
+                                                           const int32_t* __restrict__ slot_row,
+                                                           const float* __restrict__ topk_w,
+                                                           float* __restrict__ out) {
+    for (int q = 0; q < kTokensPerBlock; ++q) {
+        const int t = blockIdx.x * kTokensPerBlock + q;
+        if (t >= T) return;
+        for (int k = threadIdx.x * 8; k < H; k += kThreads * 8) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < K; ++j) {
+                const int r = slot_row[static_cast<int64_t>(t) * K + j];
+                if (r < 0) continue;
+                const float w = topk_w[static_cast<int64_t>(t) * K + j];
+                if constexpr (sizeof(YT) == 2) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(r) * H + k);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        float lo, hi;
+                        if constexpr (F16) {
+                            lo = f16_to_f32(static_cast<uint16_t>(v[d] & 0xFFFFu));
+                            hi = f16_to_f32(static_cast<uint16_t>(v[d] >> 16));
+                        } else {
+                            lo = __uint_as_float(v[d] << 16);
+                            hi = __uint_as_float(v[d] & 0xFFFF0000u);
+                        }
+                        acc[2 * d] = fmaf(w, lo, acc[2 * d]);
+                        acc[2 * d + 1] = fmaf(w, hi, acc[2 * d + 1]);
+                    }
+                } else {
+                    const floatx4 a = *reinterpret_cast<const floatx4*>(y + static_cast<int64_t>(r) * H + k);
+                    const floatx4 b = *reinterpret_cast<const floatx4*>(y + static_cast<int64_t>(r) * H + k + 4);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        acc[d] = fmaf(w, a[d], acc[d]);
+                        acc[4 + d] = fmaf(w, b[d], acc[4 + d]);
+                    }
+                }
+            }
+            float* o = out + static_cast<int64_t>(t) * H + k;
+            *reinterpret_cast<floatx4*>(o) = floatx4{acc[0], acc[1], acc[2], acc[3]};
+            *reinterpret_cast<floatx4*>(o + 4) = floatx4{acc[4], acc[5], acc[6], acc[7]};
+        }
+    }
+}
+
+}  // namespace
+
+int launch_combine(const moe_shape& s, const void* y_packed, int y_dtype, const int32_t* slot_row,
+                   const float* topk_w, float* out, hipStream_t st) {
+    const int grid = (s.T + kTokensPerBlock - 1) / kTokensPerBlock;
+    if (y_dtype == MOE_BF16)
+        hipLaunchKernelGGL((combine_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, st,
+                           static_cast<const uint16_t*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+    else if (y_dtype == MOE_F16)
+        hipLaunchKernelGGL((combine_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, st,
+                           static_cast<const uint16_t*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+    else
+        hipLaunchKernelGGL((combine_kernel<float, false>), dim3(grid), dim3(kThreads), 0, st,
+                           static_cast<const float*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,95 @@
+// Internal helpers shared by the HIP translation units of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_layer_03_amd.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+typedef _Float16 halfx8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+// Round to nearest even; saturates to +-65504 instead of overflowing to Inf.
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
+    const _Float16 h = static_cast<_Float16>(fminf(fmaxf(f, -65504.0f), 65504.0f));
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_f16_sat(lo)) | (static_cast<uint32_t>(f32_to_f16_sat(hi)) << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Kernel launch bookkeeping -------------------------------------------------
+
+// Records the hipError_t of a failed launch for moe_last_hip_error().
+void set_last_hip_error(hipError_t e);
+
+#define MOE_CHECK_LAUNCH()                                  \
+    do {                                                    \
+        hipError_t moe_err_ = hipGetLastError();            \
+        if (moe_err_ != hipSuccess) {                       \
+            ::moe::set_last_hip_error(moe_err_);            \
+            return MOE_ERR_HIP;                             \
+        }                                                   \
+    } while (0)
+
+#define MOE_TRY(expr)                                       \
+    do {                                                    \
+        int moe_st_ = (expr);                               \
+        if (moe_st_ != MOE_OK) return moe_st_;              \
+    } while (0)
+
+// Launchers (defined in the kernel translation units).  Arguments are
+// validated by the entry points before these are called.
+int launch_route(const moe_shape& s, const void* x, int x_dtype, const void* w, const float* bias,
+                 int32_t* topk_idx, float* topk_w, float* logits, hipStream_t st);
+int launch_route_from_logits(const moe_shape& s, const float* logits, int32_t* topk_idx, float* topk_w,
+                             hipStream_t st);
+
+size_t dispatch_scratch_bytes(const moe_shape& s);
+int launch_dispatch(const moe_shape& s, const int32_t* topk_idx, const void* x, int x_dtype,
+                    int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_slot,
+                    int32_t* slot_row, uint16_t* x_packed, void* scratch, hipStream_t st);
+
+size_t packed_gate_up_elems(const moe_shape& s);
+size_t packed_down_elems(const moe_shape& s);
+int launch_pack_weights(const moe_shape& s, const void* w_gate, const void* w_up, const void* w_down,
+                        int dtype, uint16_t* packed, hipStream_t st);
+// Operand type of the MFMA products: bf16 weights keep bf16, float32 weights
+// are converted to fp16; the down projection always runs in fp16.
+inline int gate_up_operand_dtype(int weight_dtype) { return weight_dtype == MOE_BF16 ? MOE_BF16 : MOE_F16; }
+int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, const int32_t* offsets,
+                        const uint16_t* packed, int which, int epilogue, void* c, int c_dtype,
+                        hipStream_t st);
+
+int launch_combine(const moe_shape& s, const void* y_packed, int y_dtype, const int32_t* slot_row,
+                   const float* topk_w, float* out, hipStream_t st);
+
+}  // namespace moe
