@@ -6,14 +6,16 @@
 // on the pages.  This library reads it as softmax over the experts, the K
 // most probable kept, their probabilities renormalised.
 //
-// Layout of the work: one wavefront owns R tokens and all E experts of those
-// tokens (lane = expert within each group of 64, NE groups).  Each lane keeps
-// R*NE float32 accumulators and runs the fused multiply-add chain over h in
-// ascending order -- the order that decides near-ties -- so the logits come
-// out identical to a sequential fmaf loop.  Router weights are staged in LDS
-// as float32 (shared by the 4 waves of the workgroup); activations are staged
-// per wave and read as LDS broadcasts.  Selection happens in registers with
-// wave-wide 64-bit max reductions over (orderable logit, ~expert) keys.
+// Every logit is one fused multiply-add chain over h in ascending order -- the
+// order that decides near-ties -- so the logits come out identical to a
+// sequential fmaf loop; that makes the router VALU work (T*E*H fma).
+// For E <= 128 a lane owns (token, expert) chains; activations and router
+// weights are staged per workgroup in LDS as float32 (double-buffered, global
+// loads running several chunks ahead through registers), so the vector unit
+// issues little besides v_fma.  Large batches give each wave 3 tokens x all
+// experts; small batches give each wave 1 token x 64 experts, the shortest
+// dependent chain, with a deeper prefetch.  Larger E uses the generic kernel.  Selection happens in registers with wave-wide
+// 64-bit max reductions over (orderable logit, ~expert) keys.
 #include "common.hpp"
 
 namespace moe {
@@ -169,6 +171,176 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// E <= 128 fast path.
+// A workgroup of WAVES waves owns TOK = (WAVES / SPLIT) * R tokens and all
+// experts.  Wave w runs R tokens against NE groups of 64 experts starting at
+// group (w % SPLIT) * NE; SPLIT = 2 lets two waves share a token (shorter
+// chains per lane for small batches).  Per HC-row chunk the workgroup stages
+// the router-weight rows (one contiguous run of HC*E elements) and the TOK
+// activation rows as float32 in LDS (double-buffered); global loads run P-1
+// chunks ahead through a register ring so their latency is covered.
+// ---------------------------------------------------------------------------
+template <typename XT, int R, int NE, int SPLIT, int WAVES, int HC, int P>
+__global__ __launch_bounds__(WAVES * 64) void route_fast_kernel(
+    const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
+    int T, int H, int E, int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits) {
+    constexpr int NT = WAVES * 64;                 // threads
+    constexpr int TOK = (WAVES / SPLIT) * R;       // tokens per workgroup
+    constexpr int VEC = 16 / sizeof(XT);           // elements per 16-byte piece
+    constexpr int WP_MAX = HC * 128 / VEC;         // router-weight pieces per chunk (E <= 128)
+    constexpr int XP = TOK * HC / VEC;             // activation pieces per chunk
+    constexpr int NPT = (WP_MAX + XP + NT - 1) / NT;   // pieces per thread per chunk
+    static_assert(HC % VEC == 0, "chunk rows must split into 16-byte pieces");
+
+    __shared__ __attribute__((aligned(16))) float s_w[2][HC * 128];
+    __shared__ __attribute__((aligned(16))) float s_x[2][TOK][HC];
+    __shared__ float s_l[SPLIT > 1 ? TOK : 1][128];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tok0 = blockIdx.x * TOK;
+    const int wtok = (wave / SPLIT) * R;           // first token of this wave (within the workgroup)
+    const int g0 = (wave % SPLIT) * NE;            // first expert group of this wave
+    const int WP = HC * E / VEC;                   // pieces of this E
+
+    // piece p < WP: router weight run; WP <= p < WP + XP: activation (token, 16-byte column);
+    // higher pieces reload piece 0.  Every thread issues the same loads with no
+    // branches, so the wait counters stay exact and the ring keeps P-1 chunks
+    // in flight.
+    auto load = [&](u32x4 (&r)[NPT], int c) {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int p = tid + i * NT;
+            const int q = p - WP;
+            const int tt = q / (HC / VEC), col = q % (HC / VEC);
+            const int t = min(tok0 + tt, T - 1);
+            const XT* src = (p < WP) ? w + static_cast<int64_t>(c) * HC * E + p * VEC
+                          : (p < WP + XP) ? x + static_cast<int64_t>(t) * H + c * HC + col * VEC
+                          : w;
+            r[i] = *reinterpret_cast<const u32x4*>(src);
+        }
+    };
+    auto store = [&](const u32x4 (&r)[NPT], int buf) {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int p = tid + i * NT;
+            float* dst;
+            if (p < WP) {
+                dst = &s_w[buf][p * VEC];
+            } else if (p < WP + XP) {
+                const int q = p - WP;
+                dst = &s_x[buf][q / (HC / VEC)][(q % (HC / VEC)) * VEC];
+            } else {
+                continue;
+            }
+            if constexpr (sizeof(XT) == 2) {
+                floatx4 a, b;
+                a[0] = __uint_as_float(r[i][0] << 16); a[1] = __uint_as_float(r[i][0] & 0xFFFF0000u);
+                a[2] = __uint_as_float(r[i][1] << 16); a[3] = __uint_as_float(r[i][1] & 0xFFFF0000u);
+                b[0] = __uint_as_float(r[i][2] << 16); b[1] = __uint_as_float(r[i][2] & 0xFFFF0000u);
+                b[2] = __uint_as_float(r[i][3] << 16); b[3] = __uint_as_float(r[i][3] & 0xFFFF0000u);
+                *reinterpret_cast<floatx4*>(dst) = a;
+                *reinterpret_cast<floatx4*>(dst + 4) = b;
+            } else {
+                *reinterpret_cast<u32x4*>(dst) = r[i];
+            }
+        }
+    };
+
+    float acc[R][NE];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int g = 0; g < NE; ++g) acc[r][g] = 0.0f;
+
+    const int nc = H / HC;
+    u32x4 ring[P][NPT];
+    // prologue: chunks 0 .. P-1 in flight, chunk 0 in LDS, slot 0 refilled with chunk P
+    // (chunk indices past the end are clamped: harmless reloads)
+#pragma unroll
+    for (int q = 0; q < P; ++q) load(ring[q], min(q, nc - 1));
+    store(ring[0], 0);
+    load(ring[0], min(P, nc - 1));
+    __syncthreads();
+
+    for (int c0 = 0; c0 < nc; c0 += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int c = c0 + q;
+            if (c >= nc) break;                     // uniform
+            const int buf = c & 1;
+            // slot (q+1) % P holds chunk c+1: it goes to the other LDS buffer (the
+            // last chunk writes an unused copy) and the slot is refilled with c+1+P
+            const int nq = (q + 1) % P;
+            store(ring[nq], buf ^ 1);
+            load(ring[nq], min(c + 1 + P, nc - 1));
+            const float* sw = s_w[buf];
+#pragma unroll
+            for (int h4 = 0; h4 < HC; h4 += 4) {
+                floatx4 xv[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) xv[r] = *reinterpret_cast<const floatx4*>(&s_x[buf][wtok + r][h4]);
+#pragma unroll
+                for (int hh = 0; hh < 4; ++hh) {
+                    float wv[NE];
+#pragma unroll
+                    for (int g = 0; g < NE; ++g) wv[g] = sw[(h4 + hh) * E + (g0 + g) * kWave + lane];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int g = 0; g < NE; ++g) acc[r][g] = fmaf(xv[r][hh], wv[g], acc[r][g]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    if constexpr (SPLIT == 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int t = tok0 + wtok + r;
+            if (t >= T) break;   // uniform across the wave
+            float l[NE];
+#pragma unroll
+            for (int g = 0; g < NE; ++g) {
+                const int e = g * kWave + lane;
+                float v = acc[r][g];
+                if (bias != nullptr && e < E) v = v + bias[e];
+                l[g] = v;
+                if (logits != nullptr && e < E) logits[static_cast<int64_t>(t) * E + e] = v;
+            }
+            select_and_write<NE>(l, E, K, t, topk_idx, topk_w);
+        }
+    } else {
+        static_assert(SPLIT * NE == 2, "split path covers 128 experts");
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int t = tok0 + wtok + r;
+#pragma unroll
+            for (int g = 0; g < NE; ++g) {
+                const int e = (g0 + g) * kWave + lane;
+                float v = acc[r][g];
+                if (bias != nullptr && e < E) v = v + bias[e];
+                if (logits != nullptr && e < E && t < T) logits[static_cast<int64_t>(t) * E + e] = v;
+                s_l[wtok + r][e] = v;
+            }
+        }
+        __syncthreads();
+        if (g0 == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int t = tok0 + wtok + r;
+                if (t >= T) break;
+                float l[2] = {s_l[wtok + r][lane], s_l[wtok + r][kWave + lane]};
+                select_and_write<2>(l, E, K, t, topk_idx, topk_w);
+            }
+        }
+    }
+}
+
 template <int NE>
 __global__ __launch_bounds__(kRouteThreads) void select_kernel(
     const float* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ topk_idx,
@@ -194,19 +366,32 @@ void launch_route_t(const moe_shape& s, const XT* x, const XT* w, const float* b
                        s.H, s.E, s.K, idx, tw, logits);
 }
 
+template <typename XT, int R, int NE, int SPLIT, int WAVES, int HC, int P>
+void launch_fast(const moe_shape& s, const XT* x, const XT* w, const float* bias, int32_t* idx, float* tw,
+                 float* logits, hipStream_t st) {
+    constexpr int TOK = (WAVES / SPLIT) * R;
+    const int grid = (s.T + TOK - 1) / TOK;
+    hipLaunchKernelGGL((route_fast_kernel<XT, R, NE, SPLIT, WAVES, HC, P>), dim3(grid), dim3(WAVES * 64), 0, st, x,
+                       w, bias, s.T, s.H, s.E, s.K, idx, tw, logits);
+}
+
 template <typename XT>
 void launch_route_dt(const moe_shape& s, const XT* x, const XT* w, const float* bias, int32_t* idx,
                      float* tw, float* logits, hipStream_t st) {
-    // Few tokens: one token per wave keeps the fma chains short per lane.
-    const bool many = s.T >= 2048;
-    if (s.E <= 64) {
-        if (many) launch_route_t<XT, 4, 1>(s, x, w, bias, idx, tw, logits, st);
-        else launch_route_t<XT, 1, 1>(s, x, w, bias, idx, tw, logits, st);
-    } else if (s.E <= 128) {
-        if (many) launch_route_t<XT, 4, 2>(s, x, w, bias, idx, tw, logits, st);
-        else launch_route_t<XT, 1, 2>(s, x, w, bias, idx, tw, logits, st);
-    } else if (s.E <= 256) {
-        if (many) launch_route_t<XT, 4, 4>(s, x, w, bias, idx, tw, logits, st);
+    if (s.E <= 128) {
+        if (s.T >= 2048) {
+            // 8 waves x 3 tokens per workgroup: about two waves per SIMD at 6000 tokens
+            if (s.E <= 64) launch_fast<XT, 3, 1, 1, 8, 32, 3>(s, x, w, bias, idx, tw, logits, st);
+            else launch_fast<XT, 3, 2, 1, 8, 32, 3>(s, x, w, bias, idx, tw, logits, st);
+        } else {
+            // one chain per lane, deep prefetch: latency-bound small batches
+            if (s.E <= 64) launch_fast<XT, 1, 1, 1, 8, 32, 8>(s, x, w, bias, idx, tw, logits, st);
+            else launch_fast<XT, 1, 1, 2, 8, 32, 8>(s, x, w, bias, idx, tw, logits, st);
+        }
+        return;
+    }
+    if (s.E <= 256) {
+        if (s.T >= 2048) launch_route_t<XT, 4, 4>(s, x, w, bias, idx, tw, logits, st);
         else launch_route_t<XT, 1, 4>(s, x, w, bias, idx, tw, logits, st);
     } else {
         launch_route_t<XT, 1, 16>(s, x, w, bias, idx, tw, logits, st);
