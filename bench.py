@@ -89,13 +89,14 @@ def main():
         row_token=torch.empty(cap, dtype=i32, device=dev),
         row_slot=torch.empty(cap, dtype=i32, device=dev),
         slot_row=torch.empty((s.T, s.K), dtype=i32, device=dev),
-        x_packed=torch.empty((cap, s.H), dtype=B.operand_dtype(x.dtype), device=dev),
+        x_packed=torch.empty((cap if wl.dtype != "bf16" else 1, s.H), dtype=B.operand_dtype(x.dtype), device=dev),
         h=torch.empty((cap, s.I), dtype=torch.float16, device=dev),
         y=torch.empty((cap, s.H), dtype=torch.float16, device=dev),
         out=torch.empty((s.T, s.H), dtype=f32, device=dev),
         ws=torch.empty(max(B.moe_dispatch_workspace_bytes(s), 16), dtype=torch.uint8, device=dev),
     )
     stages = ["route", "dispatch", "gemm_gate_up", "gemm_down", "combine"]
+    gather = wl.dtype == "bf16"
 
     def step(ev=None):
         b = buf
@@ -104,11 +105,20 @@ def main():
         B.moe_route(s, x, w_router, bias, topk_idx=b["topk_idx"], topk_w=b["topk_w"])
         if ev is not None:
             ev[1].record()
-        B.moe_dispatch(s, b["topk_idx"], x, counts=b["counts"], offsets=b["offsets"], row_token=b["row_token"],
-                       row_slot=b["row_slot"], slot_row=b["slot_row"], x_packed=b["x_packed"], ws=b["ws"])
+        if gather:   # bf16: the gate/up GEMM reads token rows straight from x, as moe_layer does
+            B.moe_dispatch(s, b["topk_idx"], None, counts=b["counts"], offsets=b["offsets"],
+                           row_token=b["row_token"], row_slot=b["row_slot"], slot_row=b["slot_row"], ws=b["ws"])
+        else:
+            B.moe_dispatch(s, b["topk_idx"], x, counts=b["counts"], offsets=b["offsets"], row_token=b["row_token"],
+                           row_slot=b["row_slot"], slot_row=b["slot_row"], x_packed=b["x_packed"], ws=b["ws"])
         if ev is not None:
             ev[2].record()
-        B.moe_grouped_gemm(s, b["x_packed"], b["offsets"], packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_SWIGLU, c=b["h"])
+        if gather:
+            B.moe_grouped_gemm(s, x, b["offsets"], packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_SWIGLU, c=b["h"],
+                               a_rows=b["row_token"])
+        else:
+            B.moe_grouped_gemm(s, b["x_packed"], b["offsets"], packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_SWIGLU,
+                               c=b["h"])
         if ev is not None:
             ev[3].record()
         B.moe_grouped_gemm(s, b["h"], b["offsets"], packed, B.MOE_GEMM_DOWN, B.MOE_EPI_NONE, c=b["y"])
@@ -176,13 +186,13 @@ def main():
         t_gu = stage_ms["gemm_gate_up"] * 1e-3
         if gu_flops / max(gu_bytes, 1) >= RIDGE:
             ach = gu_flops / t_gu / 1e12
-            roofline = dict(kernel="grouped_gemm_kernel<128,128,SwiGLU,bf16 x bf16 -> fp16> (gate/up)", bound="mfma",
+            roofline = dict(kernel="grouped_gemm_kernel<4,SwiGLU,bf16,fp16,4> (gate/up)", bound="mfma",
                             achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                             frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
                             per_launch=dict(flops=gu_flops, us=round(t_gu * 1e6, 2)))
         else:
             ach = gu_bytes / t_gu / 1e9
-            roofline = dict(kernel="grouped_gemm_kernel<128,128,SwiGLU,bf16 x bf16 -> fp16> (gate/up)", bound="hbm",
+            roofline = dict(kernel="grouped_gemm_kernel<4,SwiGLU,bf16,fp16,4> (gate/up)", bound="hbm",
                             achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                             frac=round(ach / PEAK_HBM_GBS, 4), traffic=None,
                             per_launch=dict(bytes=gu_bytes, us=round(t_gu * 1e6, 2)))

@@ -148,20 +148,24 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int
 /*
  * moe_grouped_gemm -- one GEMM problem per local expert over its packed rows
  * ("MoE GEMM"); rows [offsets[i], offsets[i+1]) use expert e_begin + i.
- *   which = MOE_GEMM_GATE_UP: a [cap, H] = x_packed, a_dtype MOE_BF16 for
- *       weights packed from bf16, MOE_F16 for weights packed from float32;
- *       epilogue MOE_EPI_SWIGLU -> c [cap, I], or MOE_EPI_NONE -> c [cap, 2I]
- *       (gate columns then up columns).
+ *   which = MOE_GEMM_GATE_UP: a_dtype MOE_BF16 for weights packed from bf16,
+ *       MOE_F16 for weights packed from float32; epilogue MOE_EPI_SWIGLU ->
+ *       c [cap, I], or MOE_EPI_NONE -> c [cap, 2I] (gate columns then up
+ *       columns).
  *   which = MOE_GEMM_DOWN: a [cap, I] fp16 (a_dtype MOE_F16); epilogue
  *       MOE_EPI_NONE -> c [cap, H].
+ *   a_rows: NULL, then a holds the packed rows ([cap, Kd]); or [cap] int32,
+ *       then packed row r is row a_rows[r] of a (for instance a = x [T, H]
+ *       and a_rows = the row_token of moe_dispatch: no packed copy needed).
  *   c_dtype MOE_F32, MOE_BF16 or MOE_F16 (16-bit outputs round to nearest
  *   even; fp16 saturates at 65504); products accumulate in float32.  Rows
  *   >= N_loc are not written.
  *   packed: the buffer moe_pack_weights() wrote for the same shape.
  *   offsets [E_loc + 1] int32, on the device (counts never visit the host).
  */
-int moe_grouped_gemm(const moe_shape* s, const uint16_t* a, int a_dtype, const int32_t* offsets, const void* packed,
-                     int which, int epilogue, void* c, int c_dtype, void* stream);
+int moe_grouped_gemm(const moe_shape* s, const uint16_t* a, int a_dtype, const int32_t* a_rows,
+                     const int32_t* offsets, const void* packed, int which, int epilogue, void* c, int c_dtype,
+                     void* stream);
 
 /*
  * moe_combine -- weighted local accumulation back to token order
@@ -189,8 +193,9 @@ int moe_combine(const moe_shape* s, const void* y_packed, int y_dtype, const int
  *       moe_dispatch.
  *   ws: moe_layer_workspace_bytes(s) bytes of device scratch.
  *   x and the packed weights must come from the same dtype.  Intermediates:
- *   packed tokens in the gate/up operand type (bf16, or fp16 for float32
- *   layers); SwiGLU activations and expert outputs in fp16.
+ *   bf16 layers read the token rows straight from x (no packed copy);
+ *   float32 layers pack them as fp16 first; SwiGLU activations and expert
+ *   outputs are fp16.
  */
 int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
               const float* bias, const void* packed, float* out,

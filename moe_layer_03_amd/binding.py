@@ -85,7 +85,8 @@ _S = ctypes.POINTER(_CShape)
 
 
 def lib_path() -> str:
-    return _build.LIB
+    """The in-tree library, or the file named by MOE_LAYER_03_AMD_LIB."""
+    return os.environ.get("MOE_LAYER_03_AMD_LIB") or _build.LIB
 
 
 def load() -> ctypes.CDLL:
@@ -108,7 +109,7 @@ def load() -> ctypes.CDLL:
         "moe_route": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P]),
         "moe_route_from_logits": (i32, [_S, _P, _P, _P, _P]),
         "moe_dispatch": (i32, [_S, _P, _P, i32, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
-        "moe_grouped_gemm": (i32, [_S, _P, i32, _P, _P, i32, i32, _P, i32, _P]),
+        "moe_grouped_gemm": (i32, [_S, _P, i32, _P, _P, _P, i32, i32, _P, i32, _P]),
         "moe_combine": (i32, [_S, _P, i32, _P, _P, _P, _P]),
         "moe_layer": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
@@ -271,8 +272,9 @@ def moe_dispatch(s: Shape, topk_idx: torch.Tensor, x: Optional[torch.Tensor] = N
 
 
 def moe_grouped_gemm(s: Shape, a: torch.Tensor, offsets: torch.Tensor, packed: torch.Tensor, which: int,
-                     epilogue: int = MOE_EPI_NONE, c=None, c_dtype=torch.float16, stream=None) -> torch.Tensor:
-    """a: bf16 or fp16 [cap, H] (gate/up) or fp16 [cap, I] (down)."""
+                     epilogue: int = MOE_EPI_NONE, c=None, c_dtype=torch.float16, a_rows=None,
+                     stream=None) -> torch.Tensor:
+    """a: bf16/fp16 packed rows [cap, Kd], or the unpacked input with a_rows [cap] int32 (row gather)."""
     cap = s.cap
     kd = s.H if which == MOE_GEMM_GATE_UP else s.I
     if which == MOE_GEMM_GATE_UP:
@@ -281,7 +283,12 @@ def moe_grouped_gemm(s: Shape, a: torch.Tensor, offsets: torch.Tensor, packed: t
         nc = s.H
     if c is None:
         c = _empty((cap, nc), c_dtype, a.device)
-    st = load().moe_grouped_gemm(ctypes.byref(s.c()), _ptr(a, None, cap * kd, "a"), _dt(a),
+    if a_rows is None and a.numel() != cap * kd:
+        raise ValueError(f"a must have {cap * kd} elements without a_rows")
+    if a.numel() % kd:
+        raise ValueError("a rows must have the reduction length")
+    st = load().moe_grouped_gemm(ctypes.byref(s.c()), _ptr(a, None, None, "a"), _dt(a),
+                                 _ptr(a_rows, torch.int32, cap, "a_rows"),
                                  _ptr(offsets, torch.int32, s.E_loc + 1, "offsets"),
                                  _ptr(packed, torch.uint8, None, "packed"), which, epilogue,
                                  _ptr(c, None, cap * nc, "c"), _dt(c), _stream(stream))

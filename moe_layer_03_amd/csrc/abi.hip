@@ -156,8 +156,8 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int
                            static_cast<hipStream_t>(stream));
 }
 
-int moe_grouped_gemm(const moe_shape* s, const uint16_t* a, int a_dtype, const int32_t* offsets, const void* packed,
-                     int which, int epilogue, void* c, int c_dtype, void* stream) {
+int moe_grouped_gemm(const moe_shape* s, const uint16_t* a, int a_dtype, const int32_t* a_rows, const int32_t* offsets,
+                     const void* packed, int which, int epilogue, void* c, int c_dtype, void* stream) {
     MOE_TRY(check_shape(s));
     if (which != MOE_GEMM_GATE_UP && which != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARG;
     if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU) return MOE_ERR_INVALID_ARG;
@@ -166,9 +166,9 @@ int moe_grouped_gemm(const moe_shape* s, const uint16_t* a, int a_dtype, const i
     if (which == MOE_GEMM_GATE_UP && a_dtype != MOE_BF16 && a_dtype != MOE_F16) return MOE_ERR_UNSUPPORTED;
     if (which == MOE_GEMM_DOWN && a_dtype != MOE_F16) return MOE_ERR_UNSUPPORTED;
     if (s->T == 0) return MOE_OK;
-    if (!ok16(a) || !ok4(offsets) || !ok16(packed) || !ok16(c)) return MOE_ERR_INVALID_ARG;
-    return launch_grouped_gemm(*s, a, a_dtype, offsets, static_cast<const uint16_t*>(packed), which, epilogue, c,
-                               c_dtype, static_cast<hipStream_t>(stream));
+    if (!ok16(a) || !opt4(a_rows) || !ok4(offsets) || !ok16(packed) || !ok16(c)) return MOE_ERR_INVALID_ARG;
+    return launch_grouped_gemm(*s, a, a_dtype, a_rows, offsets, static_cast<const uint16_t*>(packed), which,
+                               epilogue, c, c_dtype, static_cast<hipStream_t>(stream));
 }
 
 int moe_combine(const moe_shape* s, const void* y_packed, int y_dtype, const int32_t* slot_row, const float* topk_w,
@@ -213,14 +213,23 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
     int32_t* sr = slot_row ? slot_row : w.slot_row;
 
     MOE_TRY(launch_route(*s, x, x_dtype, w_router, bias, idx, tw, nullptr, st));
-    MOE_TRY(launch_dispatch(*s, idx, x, x_dtype, cnt, off, rt, rs, sr, w.x_packed, w.dispatch_scratch, st));
     const uint16_t* pk = static_cast<const uint16_t*>(packed);
-    // bf16 layers multiply in bf16 (exact inputs); float32 layers in fp16.  The
-    // SwiGLU activations and expert outputs are fp16: rounding them to bf16
-    // instead would cost about 2% of the output RMS in the largest elements.
+    // bf16 layers multiply in bf16 (exact inputs) and the gate/up GEMM gathers
+    // the token rows straight from x; float32 layers pack the rows as fp16
+    // first.  The SwiGLU activations and expert outputs are fp16: rounding them
+    // to bf16 instead would cost about 2% of the output RMS in the largest
+    // elements.
     const int op = gate_up_operand_dtype(x_dtype);
-    MOE_TRY(launch_grouped_gemm(*s, w.x_packed, op, off, pk, MOE_GEMM_GATE_UP, MOE_EPI_SWIGLU, w.h, MOE_F16, st));
-    MOE_TRY(launch_grouped_gemm(*s, w.h, MOE_F16, off, pk, MOE_GEMM_DOWN, MOE_EPI_NONE, w.y, MOE_F16, st));
+    if (x_dtype == MOE_BF16) {
+        MOE_TRY(launch_dispatch(*s, idx, nullptr, x_dtype, cnt, off, rt, rs, sr, nullptr, w.dispatch_scratch, st));
+        MOE_TRY(launch_grouped_gemm(*s, static_cast<const uint16_t*>(x), op, rt, off, pk, MOE_GEMM_GATE_UP,
+                                    MOE_EPI_SWIGLU, w.h, MOE_F16, st));
+    } else {
+        MOE_TRY(launch_dispatch(*s, idx, x, x_dtype, cnt, off, rt, rs, sr, w.x_packed, w.dispatch_scratch, st));
+        MOE_TRY(launch_grouped_gemm(*s, w.x_packed, op, nullptr, off, pk, MOE_GEMM_GATE_UP, MOE_EPI_SWIGLU, w.h,
+                                    MOE_F16, st));
+    }
+    MOE_TRY(launch_grouped_gemm(*s, w.h, MOE_F16, nullptr, off, pk, MOE_GEMM_DOWN, MOE_EPI_NONE, w.y, MOE_F16, st));
     MOE_TRY(launch_combine(*s, w.y, MOE_F16, sr, tw, out, st));
     return MOE_OK;
 }

@@ -85,9 +85,10 @@ int launch_pack_weights(const moe_shape& s, const void* w_gate, const void* w_up
 // Operand type of the MFMA products: bf16 weights keep bf16, float32 weights
 // are converted to fp16; the down projection always runs in fp16.
 inline int gate_up_operand_dtype(int weight_dtype) { return weight_dtype == MOE_BF16 ? MOE_BF16 : MOE_F16; }
-int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, const int32_t* offsets,
-                        const uint16_t* packed, int which, int epilogue, void* c, int c_dtype,
-                        hipStream_t st);
+// a_rows: NULL, or the row of `a` that packed row r reads (gather from the unpacked input)
+int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, const int32_t* a_rows,
+                        const int32_t* offsets, const uint16_t* packed, int which, int epilogue, void* c,
+                        int c_dtype, hipStream_t st);
 
 int launch_combine(const moe_shape& s, const void* y_packed, int y_dtype, const int32_t* slot_row,
                    const float* topk_w, float* out, hipStream_t st);

@@ -1,4 +1,4 @@
-// Grouped expert GEMMs on bf16 MFMA, plus the static weight packing they read.
+// Grouped expert GEMMs on MFMA, plus the static weight packing they stream.
 //
 // "Hosting Qwen on Blackwell" (Perplexity), section "MoE GEMM": the dispatched
 // tokens of each expert form one matrix-multiply problem; with about 375
@@ -7,17 +7,38 @@
 // from HBM ("Decodeurs").
 //
 // Kernel shape (gfx950):
-//   * persistent workgroups of 256 threads (4 waves in a 2x2 grid) walk a
-//     tile list laid out per expert as [n-tile][m-tile], so workgroups that
-//     run together share the same weight tile; tile ids are split into one
-//     contiguous range per XCD (workgroup b runs on XCD b % 8), keeping those
-//     sharers inside one L2;
+//   * workgroup tile = two 128-row slabs of one expert x (64 * WN) columns, with
+//     2 x WN waves (WN = 4 for the prefill shapes: 8 waves, two per SIMD, so
+//     one wave's MFMAs run while the other waits on memory); every wave owns
+//     128 rows x 64 columns: 4 x 2 tiles of v_mfma_f32_32x32x16_{bf16,f16},
+//     128 float32 accumulators per lane.  The two slabs share every weight
+//     copy; an expert's odd last slab leaves one half idle at no time cost, so
+//     rows are padded only to 128;
+//   * activation rows can be gathered straight from the unpacked input
+//     through the dispatch's row-to-token map (no packed copy);
+//   * both operands reach LDS through direct global->LDS copies (no register
+//     staging) into a ring of NB stages, so NB-1 k-tiles are always in flight;
+//     the kernel waits on its own copy counter (s_waitcnt vmcnt) and a raw
+//     barrier, since copies retire in order;
+//   * activations (A): 16-byte granules of 64-byte stage rows, XOR-swizzled by
+//     row group so fragment reads are bank-conflict free (16 lanes of a 128-bit
+//     read per pass over 64 banks); all NW waves read all 128 rows;
+//   * a stage is 32 k (24 KiB at NW = 4) and the ring is 6 deep, so about 5
+//     stages (~120 KiB per CU) are in flight: load throughput per CU is bound by
+//     bytes in flight, and this keeps it above what the MFMAs consume;
+//   * weights (B) are packed once in MFMA fragment order (one 1 KiB block per
+//     32 columns x 16 k, lane-major): every copy and every fragment read is one
+//     contiguous, conflict-free 1 KiB per wave, and each wave reads only its
+//     own columns;
+//   * fragments are read from LDS one k-step ahead of the MFMAs that use them,
+//     and the once-per-stage barrier sits between a stage's two k-steps, so it
+//     waits while MFMAs are still executing and every stage starts with its
+//     operands already in registers;
+//   * persistent workgroups walk a tile list laid out per expert as
+//     [n-tile][m-tile], so workgroups that run together share one weight
+//     tile; tile ids are split into one contiguous range per XCD (workgroup b
+//     runs on XCD b % 8), keeping those sharers inside one L2;
 //   * m-tiles per expert come from the device-side offsets (no host sync);
-//   * both operands are K-contiguous bf16 rows staged through LDS in 16-byte
-//     granules, XOR-swizzled by row so that the MFMA fragment reads are
-//     bank-conflict free; double-buffered with register prefetch;
-//   * v_mfma_f32_32x32x16_bf16 (bf16 operands) or v_mfma_f32_32x32x16_f16
-//     (fp16 operands), float32 accumulators;
 //   * epilogues: plain store (float32, bf16 or fp16), or SwiGLU for the
 //     gate/up problem, whose weights are packed so that each 64-column block
 //     holds 32 gate columns then the same 32 up columns: a lane owns g and u
@@ -32,15 +53,19 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BK = 64;                 // k per LDS stage (128 bytes of bf16 per row)
+constexpr int BM = 128;                // rows per workgroup tile
+constexpr int BK = 32;                 // k per LDS stage (64 bytes of 16-bit data per row)
+constexpr int KG = BK / 8;             // 16-byte granules per row of a stage
 constexpr int kMaxExperts = 1024;
+constexpr int kFragElems = 512;        // one 32-column x 16-k fragment block (64 lanes x 8)
 
 enum Mode { kPlain = 0, kGateUpPlain = 1, kSwiGLU = 2 };
+enum Out { kOutF32 = 0, kOutBF16 = 1, kOutF16 = 2 };
 
 struct GemmArgs {
-    const uint16_t* a;         // [rows][Kd] bf16
-    const uint16_t* b;         // [E_loc][N][Kd] bf16
+    const uint16_t* a;         // [rows][Kd] 16-bit
+    const int32_t* a_rows;     // NULL, or: packed row r reads row a_rows[r] of a (gather)
+    const uint16_t* b;         // [E_loc][N/32][Kd/16] fragment blocks
     const int32_t* offsets;    // [E_loc + 1]
     void* c;                   // output rows
     int E_loc;
@@ -50,14 +75,25 @@ struct GemmArgs {
     int I;                     // intermediate size (gate/up column remap)
 };
 
-__device__ __forceinline__ int lds_off(int row, int kg) {
-    // element offset of 16-byte granule kg (0..7) of a 64-element row
-    return row * BK + ((kg ^ (row & 7)) << 3);
+__device__ __forceinline__ int swz(int row, int kg) {
+    // Swizzled granule position of logical granule kg (0..3) of a 64-byte row.
+    // Four rows share one 256-byte bank line; XOR with (row / 4) % 4 puts the
+    // same granule of 16 consecutive rows (one ds_read_b128 pass: 16 lanes over
+    // 64 banks) in 16 distinct 4-bank groups.
+    return kg ^ ((row >> 2) & (KG - 1));
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ int lds_off(int row, int kg) {
+    // element offset of logical granule kg of a row
+    return row * BK + (swz(row, kg) << 3);
+}
 
-enum Out { kOutF32 = 0, kOutBF16 = 1, kOutF16 = 2 };
+// silu(g) = g / (1 + exp(-g)) with the hardware exp2 and reciprocal (about one
+// ulp each, far below the 16-bit rounding of the stored result).
+__device__ __forceinline__ float silu(float g) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 template <int OUT> struct OutType { typedef uint16_t type; };
 template <> struct OutType<kOutF32> { typedef float type; };
@@ -69,28 +105,28 @@ template <int OUT> __device__ __forceinline__ void store_out(typename OutType<OU
 }
 
 template <bool F16>
-__device__ __forceinline__ floatx16 mfma32(const uint16_t* a, const uint16_t* b, floatx16 c) {
+__device__ __forceinline__ floatx16 mfma32(const u32x4& a, const u32x4& b, floatx16 c) {
     if constexpr (F16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const halfx8_t*>(a),
-                                                      *reinterpret_cast<const halfx8_t*>(b), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8_t, a),
+                                                      __builtin_bit_cast(halfx8_t, b), c, 0, 0, 0);
     else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(a),
-                                                       *reinterpret_cast<const bf16x8_t*>(b), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Exclusive scan of per-expert m-tile counts into s_mt[0..E_loc], 256 threads.
-template <int BM>
+// Exclusive scan of per-expert row-unit counts (UNIT rows each) into s_mt[0..E_loc].
+template <int NTHREADS, int UNIT>
 __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E_loc, int* s_mt, int* s_tmp) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid >> 6;
-    constexpr int PER = kMaxExperts / kThreads;   // experts per thread
+    constexpr int PER = kMaxExperts / NTHREADS;   // experts per thread
     int local[PER];
     int sum = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int e = tid * PER + q;
         int v = 0;
-        if (e < E_loc) v = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+        if (e < E_loc) v = (offsets[e + 1] - offsets[e] + UNIT - 1) / UNIT;
         local[q] = v;
         sum += v;
     }
@@ -111,34 +147,58 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E_loc
         if (e <= E_loc) s_mt[e] = run;
         run += local[q];
     }
-    if (tid == kThreads - 1) s_mt[E_loc] = run;   // total (experts past E_loc add 0)
+    if (tid == NTHREADS - 1) s_mt[E_loc] = run;   // total (experts past E_loc add 0)
     __syncthreads();
 }
 
-template <int BM, int BN, int MODE, bool F16, int OUT>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
-    typedef typename OutType<OUT>::type OutT;
-    constexpr int WM = BM / 2, WN = BN / 2;      // wave tile (2x2 waves)
-    constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 MFMA tiles per wave
-    constexpr int A_LOADS = BM * 8 / kThreads;   // 16-byte granules per thread per stage
-    constexpr int B_LOADS = BN * 8 / kThreads;
-    static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
-    static_assert(MODE != kSwiGLU || (WN % 64) == 0, "SwiGLU pairs need 64-column wave tiles");
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN * BK];
+// One 16-byte-per-lane global -> LDS copy: lane l's 16 bytes from g land at
+// LDS address (wave-uniform base) + 16 * l.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                            reinterpret_cast<uintptr_t>(lds_wave_base)),
+                                     16, 0, 0);
+}
+
+template <int WN, int MODE, bool F16, int OUT, int NB>
+__global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
+    typedef typename OutType<OUT>::type OutT;
+    constexpr int NWAVES = 2 * WN;                     // 2 row halves x WN column quarters
+    constexpr int NTHREADS = NWAVES * 64;
+    constexpr int BN = WN * 64;
+    constexpr int UM = 2 * BM;                         // rows per tile: two 128-row slabs
+    constexpr int TM = BM / 32;                        // 32-row MFMA tiles per wave
+    constexpr int KS = BK / 16;                        // MFMA k-steps per stage
+    constexpr int A_GRAN = UM * KG;                    // 16-byte granules of one A stage
+    constexpr int A_DMA = A_GRAN / NTHREADS;           // A copies per thread per stage
+    constexpr int B_BLK = 2 * KS;                      // B blocks per wave column per stage
+    constexpr int B_DMA = B_BLK * WN / NWAVES;         // B copies per thread per stage
+    constexpr int LOADS = A_DMA + B_DMA;               // vector-memory operations per thread per stage
+    static_assert(A_GRAN % NTHREADS == 0 && (B_BLK * WN) % NWAVES == 0, "stage must split evenly");
+
+    __shared__ __attribute__((aligned(16))) uint16_t s_a[NB][UM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[NB][WN][B_BLK][kFragElems];
     __shared__ int s_mt[kMaxExperts + 1];
-    __shared__ int s_tmp[kThreads / kWave];
+    __shared__ int s_tmp[NWAVES];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
-    const int wm0 = (wave >> 1) * WM;
-    const int wn0 = (wave & 1) * WN;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int mh = wave / WN;                          // row half of this wave
+    const int nq = wave % WN;                          // column quarter of this wave
 
-    build_tile_prefix<BM>(p.offsets, p.E_loc, s_mt, s_tmp);
+    build_tile_prefix<NTHREADS, UM>(p.offsets, p.E_loc, s_mt, s_tmp);
     const int NT = p.N / BN;
     const int total = s_mt[p.E_loc] * NT;
+    const int nk = p.Kd / BK;
+    const int kblocks = p.Kd / 16;                     // fragment blocks per 32-column stream
 
     // contiguous tile range per XCD
     const int G = gridDim.x;
@@ -156,174 +216,211 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
         const int mt_e = s_mt[e + 1] - s_mt[e];
         const int local = tile - s_mt[e] * NT;
         const int n_tile = local / mt_e;
-        const int m_tile = local - n_tile * mt_e;
+        const int m_unit = local - n_tile * mt_e;
         const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
-        const int row0 = seg0 + m_tile * BM;
-        const int rows_valid = min(BM, seg1 - row0);
+        const int row0 = seg0 + m_unit * UM;
+        const int rows_valid = min(UM, seg1 - row0);
+        const int my_rows = rows_valid - mh * BM;      // rows of this wave's half (<= 0: idle half)
+        const bool active = my_rows > 0;
 
-        const uint16_t* __restrict__ A = p.a + static_cast<int64_t>(row0) * p.Kd;
-        const uint16_t* __restrict__ B = p.b + (static_cast<int64_t>(e) * p.N + n_tile * BN) * p.Kd;
-
-        // per-thread granule coordinates (rows past the segment read row 0 and are never stored)
-        int a_row[A_LOADS], a_kg[A_LOADS], b_row[B_LOADS], b_kg[B_LOADS];
+        // A copies of this thread: LDS granule slot (i * NWAVES + wave) * 64 + lane holds
+        // swizzled position (row, g'); the swizzle is an involution, so the logical
+        // granule is swz(row, g').  Rows past the segment copy the tile's first row
+        // (never stored).  With a_rows the row is gathered from the unpacked input.
+        const uint16_t* a_src[A_DMA];
 #pragma unroll
-        for (int s = 0; s < A_LOADS; ++s) {
-            const int g = tid + s * kThreads;
-            a_row[s] = g >> 3;
-            a_kg[s] = g & 7;
+        for (int i = 0; i < A_DMA; ++i) {
+            const int slot = (i * NWAVES + wave) * 64 + lane;
+            const int row = slot / KG;
+            const int kg = swz(row, slot % KG);
+            const int r = row0 + (row < rows_valid ? row : 0);
+            const int64_t src = p.a_rows != nullptr ? p.a_rows[r] : r;
+            a_src[i] = p.a + src * p.Kd + kg * 8;
         }
+        // B copies of this thread: blocks j = jb .. jb+B_DMA-1 of column quarter bq
+        // (block j: stream j % 2, k-step j / 2)
+        const int bq = (wave * B_DMA) / B_BLK;
+        const int jb = (wave * B_DMA) % B_BLK;
+        const uint16_t* b_src[2];
 #pragma unroll
-        for (int s = 0; s < B_LOADS; ++s) {
-            const int g = tid + s * kThreads;
-            b_row[s] = g >> 3;
-            b_kg[s] = g & 7;
-        }
-
-        u32x4 ra[A_LOADS], rb[B_LOADS];
-        auto gload = [&](int k0) {
+        for (int s2 = 0; s2 < 2; ++s2)
+            b_src[s2] = p.b + ((static_cast<int64_t>(e) * (p.N >> 5) + ((n_tile * BN + bq * 64) >> 5) + s2) * kblocks) *
+                                  kFragElems + lane * 8;
+        // issue the copies of k-tile kt into ring stage st
+        auto issue = [&](int kt, int st) {
 #pragma unroll
-            for (int s = 0; s < A_LOADS; ++s) {
-                const int r = a_row[s] < rows_valid ? a_row[s] : 0;
-                ra[s] = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(r) * p.Kd + k0 + a_kg[s] * 8);
+            for (int i = 0; i < A_DMA; ++i) dma16(a_src[i] + kt * BK, &s_a[st][(i * NWAVES + wave) * 64 * 8]);
+#pragma unroll
+            for (int d = 0; d < B_DMA; ++d) {
+                const int j = jb + d;
+                dma16(b_src[j & 1] + static_cast<int64_t>(kt * KS + (j >> 1)) * kFragElems, &s_b[st][bq][j][0]);
             }
-#pragma unroll
-            for (int s = 0; s < B_LOADS; ++s)
-                rb[s] = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(b_row[s]) * p.Kd + k0 + b_kg[s] * 8);
         };
-        auto lstore = [&](int buf) {
+        auto read_frags = [&](u32x4 (&fa)[TM], u32x4 (&fb)[2], int st, int ks) {
+            const int kg = ks * 2 + (lane >> 5);
 #pragma unroll
-            for (int s = 0; s < A_LOADS; ++s)
-                *reinterpret_cast<u32x4*>(&s_a[buf][lds_off(a_row[s], a_kg[s])]) = ra[s];
-#pragma unroll
-            for (int s = 0; s < B_LOADS; ++s)
-                *reinterpret_cast<u32x4*>(&s_b[buf][lds_off(b_row[s], b_kg[s])]) = rb[s];
+            for (int i = 0; i < TM; ++i)
+                fa[i] = *reinterpret_cast<const u32x4*>(&s_a[st][lds_off(mh * BM + i * 32 + (lane & 31), kg)]);
+            fb[0] = *reinterpret_cast<const u32x4*>(&s_b[st][nq][2 * ks][lane * 8]);
+            fb[1] = *reinterpret_cast<const u32x4*>(&s_b[st][nq][2 * ks + 1][lane * 8]);
         };
 
-        floatx16 acc[TM][TN];
+        floatx16 acc[TM][2];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-        const int nk = p.Kd / BK;
-        gload(0);
-        lstore(0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < nk) gload((kt + 1) * BK);
+        // prologue: k-tiles 0 .. NB-2 in flight (indices past the end are clamped:
+        // harmless copies keep the per-stage operation count constant)
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const int kg = ks * 2 + (lane >> 5);
-                u32x4 fa[TM], fb[TN];
+        for (int q = 0; q + 1 < NB; ++q) issue(min(q, nk - 1), q);
+
+        u32x4 fa_cur[TM], fb_cur[2], fa_nxt[TM], fb_nxt[2];
+        static_assert(KS == 2, "the stage schedule below is written for two k-steps");
+        auto mfmas = [&](const u32x4 (&fa)[TM], const u32x4 (&fb)[2]) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int r = wm0 + i * 32 + (lane & 31);
-                    fa[i] = *reinterpret_cast<const u32x4*>(&s_a[buf][lds_off(r, kg)]);
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int n = wn0 + j * 32 + (lane & 31);
-                    fb[j] = *reinterpret_cast<const u32x4*>(&s_b[buf][lds_off(n, kg)]);
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = mfma32<F16>(reinterpret_cast<const uint16_t*>(&fa[i]),
-                                                reinterpret_cast<const uint16_t*>(&fb[j]), acc[i][j]);
+            for (int i = 0; i < TM; ++i) {
+                acc[i][0] = mfma32<F16>(fa[i], fb[0], acc[i][0]);
+                acc[i][1] = mfma32<F16>(fa[i], fb[1], acc[i][1]);
             }
-            if (kt + 1 < nk) lstore(buf ^ 1);
-            __syncthreads();
+        };
+        // One k-tile from ring stage st, entered with its first k-step's fragments
+        // in fa_cur/fb_cur.  k-step 0: read k-step 1's fragments while the MFMAs
+        // run.  Then wait for this thread's copies of the next stage and meet the
+        // other waves (the next stage has landed everywhere, and nobody still reads
+        // the stage about to be refilled) while those MFMAs drain; refill that stage
+        // with k-tile kt+NB-1.  k-step 1: read the next stage's first fragments
+        // while its MFMAs run.  An idle half only copies and synchronises.
+        auto step = [&](int kt, int st) {
+            if (active) {
+                read_frags(fa_nxt, fb_nxt, st, 1);
+                mfmas(fa_cur, fb_cur);
+            }
+            wait_vmcnt<LOADS * (NB - 3)>();
+            __builtin_amdgcn_s_barrier();
+            issue(min(kt + NB - 1, nk - 1), (st + NB - 1) % NB);
+            if (active) {
+                read_frags(fa_cur, fb_cur, (st + 1) % NB, 0);
+                mfmas(fa_nxt, fb_nxt);
+            }
+        };
+        // stage 0 must have landed before its first fragments are read
+        wait_vmcnt<LOADS * (NB - 2)>();
+        __builtin_amdgcn_s_barrier();
+        if (active) read_frags(fa_cur, fb_cur, 0, 0);
+        int kt0 = 0;
+        for (; kt0 + NB <= nk; kt0 += NB) {
+#pragma unroll
+            for (int q = 0; q < NB; ++q) step(kt0 + q, q);
         }
+#pragma unroll
+        for (int q = 0; q + 1 < NB; ++q)
+            if (kt0 + q < nk) step(kt0 + q, q);
 
         // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 tile
-        OutT* __restrict__ C = static_cast<OutT*>(p.c);
+        if (active) {
+            OutT* __restrict__ C = static_cast<OutT*>(p.c);
+            const int pc0 = n_tile * BN + nq * 64;   // packed column of acc[.][0] (multiple of 64)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = wm0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (r >= rows_valid) continue;
-                OutT* crow = C + static_cast<int64_t>(row0 + r) * p.ldc;
-                if constexpr (MODE == kSwiGLU) {
-#pragma unroll
-                    for (int j = 0; j < TN; j += 2) {
-                        const int pc = n_tile * BN + wn0 + j * 32;   // multiple of 64: gate block start
-                        const int col = (pc >> 1) + (lane & 31);
-                        store_out<OUT>(crow + col, silu(acc[i][j][v]) * acc[i][j + 1][v]);
-                    }
-                } else if constexpr (MODE == kGateUpPlain) {
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        const int pc = n_tile * BN + wn0 + j * 32 + (lane & 31);
-                        const int q = pc >> 6, w = pc & 63;
-                        const int col = w < 32 ? q * 32 + w : p.I + q * 32 + (w - 32);
-                        store_out<OUT>(crow + col, acc[i][j][v]);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        const int col = n_tile * BN + wn0 + j * 32 + (lane & 31);
-                        store_out<OUT>(crow + col, acc[i][j][v]);
+                for (int v = 0; v < 16; ++v) {
+                    const int r = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    if (r >= my_rows) continue;
+                    OutT* crow = C + static_cast<int64_t>(row0 + mh * BM + r) * p.ldc;
+                    if constexpr (MODE == kSwiGLU) {
+                        const int col = (pc0 >> 1) + (lane & 31);
+                        store_out<OUT>(crow + col, silu(acc[i][0][v]) * acc[i][1][v]);
+                    } else if constexpr (MODE == kGateUpPlain) {
+                        const int q = pc0 >> 6, w = lane & 31;
+                        store_out<OUT>(crow + q * 32 + w, acc[i][0][v]);
+                        store_out<OUT>(crow + p.I + q * 32 + w, acc[i][1][v]);
+                    } else {
+                        store_out<OUT>(crow + pc0 + (lane & 31), acc[i][0][v]);
+                        store_out<OUT>(crow + pc0 + 32 + (lane & 31), acc[i][1][v]);
                     }
                 }
             }
         }
-        __syncthreads();   // LDS reuse by the next tile
+        __syncthreads();   // LDS reuse by the next tile; drains this tile's copies
     }
 }
 
 // ---------------------------------------------------------------------------
-// weight packing: [E_loc][R][Cs] (row-major, y = x W) -> [E_loc][Cs'][R] 16-bit,
-// rows of the output are the GEMM's N index, K-contiguous.
-// gate/up: output row p of 2I, 64-blocks of (32 gate | 32 up) columns.
+// Weight packing into MFMA fragment order.
+// Source [E_loc][Kd][Cs] row-major (y = x W: k is the row, the output column c
+// the column).  Output column c maps to packed column pcol(c): identity for
+// the down weights; 64-blocks of (32 gate | 32 up) columns for gate/up.
+// Fragment block (n32, k16) holds, for lane l and j < 8, the element
+// (k = k16*16 + (l/32)*8 + j, packed column n32*32 + l%32); blocks of one
+// 32-column stream are contiguous along k.
+// One thread gathers the 8 k-consecutive values of one source column.
 // ---------------------------------------------------------------------------
-template <typename ST, bool GATE_UP, bool F16OUT>
-__global__ __launch_bounds__(256) void pack_kernel(const ST* __restrict__ src, int R, int Cs, int I,
-                                                   bool is_up, uint16_t* __restrict__ dst, int dst_rows) {
-    __shared__ float tile[64][65];
+template <typename ST, bool F16OUT>
+__global__ __launch_bounds__(256) void pack_weights_kernel(const ST* __restrict__ src, int Kd, int Cs, int N,
+                                                           int gate_up, int is_up, uint16_t* __restrict__ dst) {
     const int e = blockIdx.z;
-    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-    const ST* s = src + static_cast<int64_t>(e) * R * Cs;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int rr = i / 64, cc = i % 64;
-        float v;
-        if constexpr (sizeof(ST) == 2) v = bf16_to_f32(s[static_cast<int64_t>(r0 + rr) * Cs + c0 + cc]);
-        else v = s[static_cast<int64_t>(r0 + rr) * Cs + c0 + cc];
-        tile[rr][cc] = v;
+    const int k8 = blockIdx.y;                         // group of 8 consecutive k
+    const int c = blockIdx.x * 256 + threadIdx.x;      // source column
+    if (c >= Cs) return;
+    const ST* s = src + (static_cast<int64_t>(e) * Kd + k8 * 8) * Cs + c;
+    uint16_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float f;
+        if constexpr (sizeof(ST) == 2) f = bf16_to_f32(s[static_cast<int64_t>(j) * Cs]);
+        else f = s[static_cast<int64_t>(j) * Cs];
+        v[j] = F16OUT ? f32_to_f16_sat(f) : f32_to_bf16(f);
     }
-    __syncthreads();
-    uint16_t* d = dst + static_cast<int64_t>(e) * dst_rows * R;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int cc = i / 64, rr = i % 64;
-        const int c = c0 + cc;
-        int prow = c;
-        if constexpr (GATE_UP) prow = (c >> 5) * 64 + (is_up ? 32 : 0) + (c & 31);
-        const float v = tile[rr][cc];
-        d[static_cast<int64_t>(prow) * R + r0 + rr] = F16OUT ? f32_to_f16_sat(v) : f32_to_bf16(v);
-    }
+    const int pcol = gate_up ? (c >> 5) * 64 + (is_up ? 32 : 0) + (c & 31) : c;
+    const int n32 = pcol >> 5;
+    const int lanei = (pcol & 31) + 32 * (k8 & 1);
+    const int k16 = k8 >> 1;
+    uint16_t* d = dst + ((static_cast<int64_t>(e) * (N >> 5) + n32) * (Kd >> 4) + k16) * kFragElems + lanei * 8;
+    u32x4 o;
+    o[0] = v[0] | (static_cast<uint32_t>(v[1]) << 16);
+    o[1] = v[2] | (static_cast<uint32_t>(v[3]) << 16);
+    o[2] = v[4] | (static_cast<uint32_t>(v[5]) << 16);
+    o[3] = v[6] | (static_cast<uint32_t>(v[7]) << 16);
+    *reinterpret_cast<u32x4*>(d) = o;
 }
 
-template <int BM, int BN, int MODE, bool F16, int OUT>
+template <int WN, int MODE, bool F16, int OUT>
 int launch_gemm_t(const GemmArgs& args, int max_rows, hipStream_t st) {
-    // upper bound of tiles: each expert adds at most one partial m-tile
-    const int64_t mt_bound = (static_cast<int64_t>(max_rows) + BM - 1) / BM + args.E_loc;
-    const int64_t tiles = mt_bound * (args.N / BN);
+    constexpr int NB = 4;
+    constexpr int BN = WN * 64;
+    // upper bound of tiles: each expert adds at most one partial row unit
+    const int64_t units = (static_cast<int64_t>(max_rows) + 2 * BM - 1) / (2 * BM) + args.E_loc;
+    const int64_t tiles = units * (args.N / BN);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    int64_t grid = 2LL * cus;
+    int64_t grid = static_cast<int64_t>(cus) * (4 / WN);   // one workgroup per CU at WN = 4
     if (tiles < grid) grid = tiles;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, MODE, F16, OUT>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kThreads), 0, st, args);
+    hipLaunchKernelGGL((grouped_gemm_kernel<WN, MODE, F16, OUT, NB>), dim3(static_cast<unsigned>(grid)),
+                       dim3(WN * 128), 0, st, args);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
+}
+
+template <int MODE, bool F16, int OUT>
+int launch_nw(const GemmArgs& args, int max_rows, hipStream_t st) {
+    if (args.N % 256 == 0) return launch_gemm_t<4, MODE, F16, OUT>(args, max_rows, st);
+    if (args.N % 128 == 0) return launch_gemm_t<2, MODE, F16, OUT>(args, max_rows, st);
+    return launch_gemm_t<1, MODE, F16, OUT>(args, max_rows, st);
+}
+
+template <int MODE, bool F16>
+int launch_out(const GemmArgs& args, int max_rows, int c_dtype, hipStream_t st) {
+    if (c_dtype == MOE_F32) return launch_nw<MODE, F16, kOutF32>(args, max_rows, st);
+    if (c_dtype == MOE_BF16) return launch_nw<MODE, F16, kOutBF16>(args, max_rows, st);
+    return launch_nw<MODE, F16, kOutF16>(args, max_rows, st);
 }
 
 }  // namespace
@@ -340,49 +437,36 @@ int launch_pack_weights(const moe_shape& s, const void* w_gate, const void* w_up
     const int E_loc = s.e_end - s.e_begin;
     uint16_t* gu = packed;
     uint16_t* dn = packed + packed_gate_up_elems(s);
-    const dim3 g_gu(s.I / 64, s.H / 64, E_loc), g_dn(s.H / 64, s.I / 64, E_loc);
+    const dim3 g_gu((s.I + 255) / 256, s.H / 8, E_loc), g_dn((s.H + 255) / 256, s.I / 8, E_loc);
     if (dtype == MOE_BF16) {
         auto g = static_cast<const uint16_t*>(w_gate);
         auto u = static_cast<const uint16_t*>(w_up);
         auto d = static_cast<const uint16_t*>(w_down);
-        hipLaunchKernelGGL((pack_kernel<uint16_t, true, false>), g_gu, dim3(256), 0, st, g, s.H, s.I, s.I, false, gu,
-                           2 * s.I);
-        hipLaunchKernelGGL((pack_kernel<uint16_t, true, false>), g_gu, dim3(256), 0, st, u, s.H, s.I, s.I, true, gu,
-                           2 * s.I);
-        hipLaunchKernelGGL((pack_kernel<uint16_t, false, true>), g_dn, dim3(256), 0, st, d, s.I, s.H, s.I, false, dn,
-                           s.H);
+        hipLaunchKernelGGL((pack_weights_kernel<uint16_t, false>), g_gu, dim3(256), 0, st, g, s.H, s.I, 2 * s.I, 1, 0,
+                           gu);
+        hipLaunchKernelGGL((pack_weights_kernel<uint16_t, false>), g_gu, dim3(256), 0, st, u, s.H, s.I, 2 * s.I, 1, 1,
+                           gu);
+        hipLaunchKernelGGL((pack_weights_kernel<uint16_t, true>), g_dn, dim3(256), 0, st, d, s.I, s.H, s.H, 0, 0, dn);
     } else {
         auto g = static_cast<const float*>(w_gate);
         auto u = static_cast<const float*>(w_up);
         auto d = static_cast<const float*>(w_down);
-        hipLaunchKernelGGL((pack_kernel<float, true, true>), g_gu, dim3(256), 0, st, g, s.H, s.I, s.I, false, gu,
-                           2 * s.I);
-        hipLaunchKernelGGL((pack_kernel<float, true, true>), g_gu, dim3(256), 0, st, u, s.H, s.I, s.I, true, gu,
-                           2 * s.I);
-        hipLaunchKernelGGL((pack_kernel<float, false, true>), g_dn, dim3(256), 0, st, d, s.I, s.H, s.I, false, dn,
-                           s.H);
+        hipLaunchKernelGGL((pack_weights_kernel<float, true>), g_gu, dim3(256), 0, st, g, s.H, s.I, 2 * s.I, 1, 0, gu);
+        hipLaunchKernelGGL((pack_weights_kernel<float, true>), g_gu, dim3(256), 0, st, u, s.H, s.I, 2 * s.I, 1, 1, gu);
+        hipLaunchKernelGGL((pack_weights_kernel<float, true>), g_dn, dim3(256), 0, st, d, s.I, s.H, s.H, 0, 0, dn);
     }
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
 
-namespace {
-
-template <int BM, int BN, int MODE, bool F16>
-int launch_out(const GemmArgs& args, int max_rows, int c_dtype, hipStream_t st) {
-    if (c_dtype == MOE_F32) return launch_gemm_t<BM, BN, MODE, F16, kOutF32>(args, max_rows, st);
-    if (c_dtype == MOE_BF16) return launch_gemm_t<BM, BN, MODE, F16, kOutBF16>(args, max_rows, st);
-    return launch_gemm_t<BM, BN, MODE, F16, kOutF16>(args, max_rows, st);
-}
-
-}  // namespace
-
-int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, const int32_t* offsets,
-                        const uint16_t* packed, int which, int epilogue, void* c, int c_dtype, hipStream_t st) {
+int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, const int32_t* a_rows,
+                        const int32_t* offsets, const uint16_t* packed, int which, int epilogue, void* c, int c_dtype,
+                        hipStream_t st) {
     const int E_loc = s.e_end - s.e_begin;
     const int max_rows = s.T * (s.K < E_loc ? s.K : E_loc);
     GemmArgs args;
     args.a = a;
+    args.a_rows = a_rows;
     args.offsets = offsets;
     args.c = c;
     args.E_loc = E_loc;
@@ -394,17 +478,16 @@ int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, cons
         args.ldc = epilogue == MOE_EPI_SWIGLU ? s.I : 2 * s.I;
         const bool f16 = a_dtype == MOE_F16;
         if (epilogue == MOE_EPI_SWIGLU)
-            return f16 ? launch_out<128, 128, kSwiGLU, true>(args, max_rows, c_dtype, st)
-                       : launch_out<128, 128, kSwiGLU, false>(args, max_rows, c_dtype, st);
-        return f16 ? launch_out<128, 128, kGateUpPlain, true>(args, max_rows, c_dtype, st)
-                   : launch_out<128, 128, kGateUpPlain, false>(args, max_rows, c_dtype, st);
+            return f16 ? launch_out<kSwiGLU, true>(args, max_rows, c_dtype, st)
+                       : launch_out<kSwiGLU, false>(args, max_rows, c_dtype, st);
+        return f16 ? launch_out<kGateUpPlain, true>(args, max_rows, c_dtype, st)
+                   : launch_out<kGateUpPlain, false>(args, max_rows, c_dtype, st);
     }
     args.b = packed + packed_gate_up_elems(s);
     args.N = s.H;
     args.Kd = s.I;
     args.ldc = s.H;
-    if (s.H % 128 == 0) return launch_out<128, 128, kPlain, true>(args, max_rows, c_dtype, st);
-    return launch_out<128, 64, kPlain, true>(args, max_rows, c_dtype, st);
+    return launch_out<kPlain, true>(args, max_rows, c_dtype, st);
 }
 
 }  // namespace moe

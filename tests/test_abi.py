@@ -79,12 +79,13 @@ def test_invalid_pointers_and_enums():
     assert lib.moe_route(S, p16, B.MOE_BF16, p16, B.MOE_F32, None, p16, p16, None, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_route(S, p16, 7, p16, 7, None, p16, p16, None, None) == B.MOE_ERR_UNSUPPORTED
     G = lib.moe_grouped_gemm
-    assert G(S, p16, B.MOE_BF16, p16, p16, 5, 0, p16, B.MOE_BF16, None) == B.MOE_ERR_INVALID_ARG
-    assert G(S, p16, B.MOE_F16, p16, p16, B.MOE_GEMM_DOWN, B.MOE_EPI_SWIGLU, p16, B.MOE_BF16,
+    assert G(S, p16, B.MOE_BF16, None, p16, p16, 5, 0, p16, B.MOE_BF16, None) == B.MOE_ERR_INVALID_ARG
+    assert G(S, p16, B.MOE_F16, None, p16, p16, B.MOE_GEMM_DOWN, B.MOE_EPI_SWIGLU, p16, B.MOE_BF16,
              None) == B.MOE_ERR_INVALID_ARG
-    assert G(S, p16, B.MOE_BF16, p16, p16, 0, 0, p16, 9, None) == B.MOE_ERR_UNSUPPORTED
-    assert G(S, p16, B.MOE_BF16, p16, p16, B.MOE_GEMM_DOWN, 0, p16, B.MOE_F16, None) == B.MOE_ERR_UNSUPPORTED
-    assert G(S, p16, B.MOE_F32, p16, p16, B.MOE_GEMM_GATE_UP, 0, p16, B.MOE_F16, None) == B.MOE_ERR_UNSUPPORTED
+    assert G(S, p16, B.MOE_BF16, None, p16, p16, 0, 0, p16, 9, None) == B.MOE_ERR_UNSUPPORTED
+    assert G(S, p16, B.MOE_BF16, None, p16, p16, B.MOE_GEMM_DOWN, 0, p16, B.MOE_F16, None) == B.MOE_ERR_UNSUPPORTED
+    assert G(S, p16, B.MOE_F32, None, p16, p16, B.MOE_GEMM_GATE_UP, 0, p16, B.MOE_F16, None) == B.MOE_ERR_UNSUPPORTED
+    assert G(S, p16, B.MOE_BF16, odd, p16, p16, 0, 0, p16, B.MOE_F16, None) == B.MOE_ERR_INVALID_ARG
     need = lib.moe_dispatch_workspace_bytes(S)
     assert need > 0
     assert lib.moe_dispatch(S, p16, None, 0, p16, p16, p16, p16, p16, None, p16, need - 1,
