@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the timed region, run a plain device copy (torch.neg) of this many MiB twice, "
+                         "so a counter run can scale FETCH_SIZE/WRITE_SIZE against a kernel of known traffic")
     return ap.parse_args()
 
 
@@ -128,6 +131,15 @@ def main():
         if ev is not None:
             ev[5].record()
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.randn(n, dtype=f32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -188,13 +200,13 @@ def main():
             ach = gu_flops / t_gu / 1e12
             roofline = dict(kernel="grouped_gemm_kernel<4,SwiGLU,bf16,fp16,4> (gate/up)", bound="mfma",
                             achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                            frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
+                            frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(wl.name),
                             per_launch=dict(flops=gu_flops, us=round(t_gu * 1e6, 2)))
         else:
             ach = gu_bytes / t_gu / 1e9
             roofline = dict(kernel="grouped_gemm_kernel<4,SwiGLU,bf16,fp16,4> (gate/up)", bound="hbm",
                             achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                            frac=round(ach / PEAK_HBM_GBS, 4), traffic=None,
+                            frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(wl.name),
                             per_launch=dict(bytes=gu_bytes, us=round(t_gu * 1e6, 2)))
 
     cpu = None
@@ -230,6 +242,30 @@ def main():
         "input_setup_s": round(t_gen, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate/up GEMM launch from the committed counter summary of this workload, or None.
+
+    The summary's ``traffic:`` line holds FETCH_SIZE/WRITE_SIZE scaled by a plain copy of known size, and a
+    SHA-256 of the kernel sources at the time of the counter runs: a kernel changed since then gives None.
+    """
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic: kernel=gate_up read_bytes=(\d+) write_bytes=(\d+) sources_sha256=([0-9a-f]+)$",
+                  open(path).read(), re.M)
+    if not m:
+        return None
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "moe_layer_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != m.group(3):
+        return None
+    return int(m.group(1)) + int(m.group(2))
 
 
 def cpu_baseline(wl, inp, n_tokens):

@@ -20,7 +20,7 @@ layer, as "Hosting Qwen on Blackwell" (Perplexity) states the problem:
   token order; the rank's result is the partial sum that the cross-rank
   all-reduce would add up ("Expert Parallel").
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * router: softmax over all E experts, keep the K largest, renormalise them to
   sum to one;
