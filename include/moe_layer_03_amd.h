@@ -76,6 +76,14 @@ typedef struct moe_shape {
 /* Bytes of scratch memory moe_dispatch() needs (host-only, no HIP call). */
 size_t moe_dispatch_workspace_bytes(const moe_shape* s);
 
+/*
+ * Bytes of scratch memory that let moe_route() take its screened path
+ * (host-only, no HIP call): bf16 inputs, E == 128, T >= 512, H a multiple
+ * of 128 and at most 65536, no logits output.  0 when the shape cannot take
+ * it.
+ */
+size_t moe_route_workspace_bytes(const moe_shape* s);
+
 /* Bytes of scratch memory moe_layer() needs (host-only, no HIP call). */
 size_t moe_layer_workspace_bytes(const moe_shape* s);
 
@@ -112,9 +120,17 @@ int moe_pack_weights(const moe_shape* s, const void* w_gate, const void* w_up, c
  *       equal logits (-0 == +0) ordered by ascending expert index.
  *   topk_w (output) [T, K] float32: exp(l_j - l_0) / sum_i exp(l_i - l_0)
  *       over the chosen K, i.e. the softmax probabilities renormalised.
+ *   ws, ws_bytes: scratch memory, or NULL.  With ws != NULL (16-byte aligned,
+ *       ws_bytes >= moe_route_workspace_bytes(s), else MOE_ERR_WORKSPACE) and
+ *       a shape that allows it, logits are first estimated with bf16 MFMA and
+ *       only the experts a rigorous error bound cannot exclude from the top K
+ *       are evaluated in the fma chain above; the outputs are identical to
+ *       evaluating every logit, which is what happens with ws == NULL or
+ *       when logits are requested.
  */
 int moe_route(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
-              const float* bias, int32_t* topk_idx, float* topk_w, float* logits, void* stream);
+              const float* bias, int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
+              void* stream);
 
 /*
  * moe_route_from_logits -- the selection and weighting step of moe_route on

@@ -36,7 +36,8 @@ MOE_EPI_NONE = 0
 MOE_EPI_SWIGLU = 1
 
 EXPORTED = [
-    "moe_dispatch_workspace_bytes", "moe_layer_workspace_bytes", "moe_packed_weight_bytes",
+    "moe_dispatch_workspace_bytes", "moe_route_workspace_bytes", "moe_layer_workspace_bytes",
+    "moe_packed_weight_bytes",
     "moe_pack_weights", "moe_route", "moe_route_from_logits", "moe_dispatch", "moe_grouped_gemm",
     "moe_combine", "moe_layer", "moe_status_string", "moe_last_hip_error",
 ]
@@ -103,10 +104,11 @@ def load() -> ctypes.CDLL:
     i32 = ctypes.c_int
     sigs = {
         "moe_dispatch_workspace_bytes": (sz, [_S]),
+        "moe_route_workspace_bytes": (sz, [_S]),
         "moe_layer_workspace_bytes": (sz, [_S]),
         "moe_packed_weight_bytes": (sz, [_S]),
         "moe_pack_weights": (i32, [_S, _P, _P, _P, i32, _P, _P]),
-        "moe_route": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P]),
+        "moe_route": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P, sz, _P]),
         "moe_route_from_logits": (i32, [_S, _P, _P, _P, _P]),
         "moe_dispatch": (i32, [_S, _P, _P, i32, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_grouped_gemm": (i32, [_S, _P, i32, _P, _P, _P, i32, i32, _P, i32, _P]),
@@ -184,6 +186,10 @@ def moe_dispatch_workspace_bytes(s: Shape) -> int:
     return int(load().moe_dispatch_workspace_bytes(ctypes.byref(s.c())))
 
 
+def moe_route_workspace_bytes(s: Shape) -> int:
+    return int(load().moe_route_workspace_bytes(ctypes.byref(s.c())))
+
+
 def moe_layer_workspace_bytes(s: Shape) -> int:
     return int(load().moe_layer_workspace_bytes(ctypes.byref(s.c())))
 
@@ -210,8 +216,12 @@ def moe_pack_weights(s: Shape, w_gate: torch.Tensor, w_up: torch.Tensor, w_down:
 
 
 def moe_route(s: Shape, x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor] = None,
-              topk_idx=None, topk_w=None, logits=None, want_logits=False, stream=None):
-    """Returns (topk_idx int32 [T,K], topk_w fp32 [T,K], logits fp32 [T,E] or None)."""
+              topk_idx=None, topk_w=None, logits=None, want_logits=False, ws=None, screened=True, stream=None):
+    """Returns (topk_idx int32 [T,K], topk_w fp32 [T,K], logits fp32 [T,E] or None).
+
+    ``screened=False`` passes no workspace, so every logit is evaluated in its
+    fma chain; with the default the library screens when the shape allows it
+    (the outputs are the same)."""
     dev = x.device
     if topk_idx is None:
         topk_idx = _empty((s.T, s.K), torch.int32, dev)
@@ -219,11 +229,17 @@ def moe_route(s: Shape, x: torch.Tensor, w_router: torch.Tensor, bias: Optional[
         topk_w = _empty((s.T, s.K), torch.float32, dev)
     if logits is None and want_logits:
         logits = _empty((s.T, s.E), torch.float32, dev)
+    if not screened:
+        ws = None
+    elif ws is None:
+        need = moe_route_workspace_bytes(s)
+        ws = _empty(need, torch.uint8, dev) if need > 0 else None
     st = load().moe_route(ctypes.byref(s.c()), _ptr(x, None, s.T * s.H, "x"), _dt(x),
                           _ptr(w_router, None, s.H * s.E, "w_router"), _dt(w_router),
                           _ptr(bias, torch.float32, s.E, "bias"), _ptr(topk_idx, torch.int32, s.T * s.K, "topk_idx"),
                           _ptr(topk_w, torch.float32, s.T * s.K, "topk_w"),
-                          _ptr(logits, torch.float32, s.T * s.E, "logits"), _stream(stream))
+                          _ptr(logits, torch.float32, s.T * s.E, "logits"),
+                          _ptr(ws, torch.uint8, None, "ws"), ws.numel() if ws is not None else 0, _stream(stream))
     _check("moe_route", st)
     return topk_idx, topk_w, logits
 

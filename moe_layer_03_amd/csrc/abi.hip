@@ -51,6 +51,8 @@ struct LayerWs {
     int32_t* row_slot;
     int32_t* slot_row;
     void* dispatch_scratch;
+    void* route_scratch;  // screened router (bf16 layers with 128 experts)
+    size_t route_bytes;
     uint16_t* x_packed;
     uint16_t* h;      // SwiGLU activations, fp16
     uint16_t* y;      // expert outputs, fp16
@@ -77,6 +79,8 @@ LayerWs carve_layer(const moe_shape& s, void* base) {
     w.row_slot = reinterpret_cast<int32_t*>(take(cap * 4));
     w.slot_row = reinterpret_cast<int32_t*>(take(TK * 4));
     w.dispatch_scratch = take(dispatch_scratch_bytes(s));
+    w.route_bytes = route_screen_bytes(s, MOE_BF16, MOE_BF16);
+    w.route_scratch = take(w.route_bytes);
     w.x_packed = reinterpret_cast<uint16_t*>(take(cap * s.H * 2));
     w.h = reinterpret_cast<uint16_t*>(take(cap * s.I * 2));
     w.y = reinterpret_cast<uint16_t*>(take(cap * s.H * 2));
@@ -99,6 +103,11 @@ size_t moe_dispatch_workspace_bytes(const moe_shape* s) {
     return dispatch_scratch_bytes(*s);
 }
 
+size_t moe_route_workspace_bytes(const moe_shape* s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return route_screen_bytes(*s, MOE_BF16, MOE_BF16);
+}
+
 size_t moe_layer_workspace_bytes(const moe_shape* s) {
     if (check_shape(s) != MOE_OK) return 0;
     return carve_layer(*s, nullptr).bytes;
@@ -119,14 +128,19 @@ int moe_pack_weights(const moe_shape* s, const void* w_gate, const void* w_up, c
 }
 
 int moe_route(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype, const float* bias,
-              int32_t* topk_idx, float* topk_w, float* logits, void* stream) {
+              int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes, void* stream) {
     MOE_TRY(check_shape(s));
     if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype)) return MOE_ERR_UNSUPPORTED;
     if (x_dtype != w_dtype) return MOE_ERR_UNSUPPORTED;
+    if (ws != nullptr) {
+        if (!aligned(ws, 16)) return MOE_ERR_INVALID_ARG;
+        if (ws_bytes < route_screen_bytes(*s, x_dtype, w_dtype)) return MOE_ERR_WORKSPACE;
+    }
     if (s->T == 0) return MOE_OK;   // nothing to route; empty tensors may have null pointers
     if (!ok16(x) || !ok16(w_router) || !ok4(topk_idx) || !ok4(topk_w) || !opt4(bias) || !opt4(logits))
         return MOE_ERR_INVALID_ARG;
-    return launch_route(*s, x, x_dtype, w_router, bias, topk_idx, topk_w, logits, static_cast<hipStream_t>(stream));
+    return launch_route(*s, x, x_dtype, w_router, bias, topk_idx, topk_w, logits, ws, ws_bytes,
+                        static_cast<hipStream_t>(stream));
 }
 
 int moe_route_from_logits(const moe_shape* s, const float* logits, int32_t* topk_idx, float* topk_w,
@@ -212,7 +226,7 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
     int32_t* rs = row_slot ? row_slot : w.row_slot;
     int32_t* sr = slot_row ? slot_row : w.slot_row;
 
-    MOE_TRY(launch_route(*s, x, x_dtype, w_router, bias, idx, tw, nullptr, st));
+    MOE_TRY(launch_route(*s, x, x_dtype, w_router, bias, idx, tw, nullptr, w.route_scratch, w.route_bytes, st));
     const uint16_t* pk = static_cast<const uint16_t*>(packed);
     // bf16 layers multiply in bf16 (exact inputs) and the gate/up GEMM gathers
     // the token rows straight from x; float32 layers pack the rows as fp16

@@ -46,6 +46,41 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// Asynchronous global -> LDS copies ------------------------------------------
+//
+// The compiler does not track which LDS bytes a direct-to-LDS copy writes, so
+// kernels that use dma16() order them by hand: wait_vmcnt<N>() (at most N of
+// this wave's vector-memory operations still in flight; they retire in order)
+// followed by a workgroup barrier before the staged data is read.
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Same with a wave-uniform run-time bound n, LO <= n < HI (a binary search
+// over the immediate encodings: log2(HI - LO) scalar branches).
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_bin(int n) {
+    if constexpr (HI - LO == 1) {
+        wait_vmcnt<LO>();
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        if (n < MID) wait_vmcnt_bin<LO, MID>(n);
+        else wait_vmcnt_bin<MID, HI>(n);
+    }
+}
+
+// One 16-byte-per-lane global -> LDS copy: lane l's 16 bytes from g land at
+// LDS address (wave-uniform base) + 16 * l.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                            reinterpret_cast<uintptr_t>(lds_wave_base)),
+                                     16, 0, 0);
+}
+
 // Kernel launch bookkeeping -------------------------------------------------
 
 // Records the hipError_t of a failed launch for moe_last_hip_error().
@@ -68,8 +103,9 @@ void set_last_hip_error(hipError_t e);
 
 // Launchers (defined in the kernel translation units).  Arguments are
 // validated by the entry points before these are called.
+size_t route_screen_bytes(const moe_shape& s, int x_dtype, int w_dtype);
 int launch_route(const moe_shape& s, const void* x, int x_dtype, const void* w, const float* bias,
-                 int32_t* topk_idx, float* topk_w, float* logits, hipStream_t st);
+                 int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes, hipStream_t st);
 int launch_route_from_logits(const moe_shape& s, const float* logits, int32_t* topk_idx, float* topk_w,
                              hipStream_t st);
 

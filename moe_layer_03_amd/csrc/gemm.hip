@@ -153,20 +153,6 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E_loc
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// One 16-byte-per-lane global -> LDS copy: lane l's 16 bytes from g land at
-// LDS address (wave-uniform base) + 16 * l.
-__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                            reinterpret_cast<uintptr_t>(lds_wave_base)),
-                                     16, 0, 0);
-}
-
 template <int WN, int MODE, bool F16, int OUT, int NB>
 __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
     typedef typename OutType<OUT>::type OutT;

@@ -398,11 +398,584 @@ void launch_route_dt(const moe_shape& s, const XT* x, const XT* w, const float* 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Screened path: bf16 activations and router weights, E == 128, no logits
+// output.  Two kernels:
+//
+//  1. route_screen_kernel -- estimates every logit with bf16 MFMA (any
+//     summation order) over one H slice, together with the squared norms of
+//     the token rows and of the router-weight columns, and writes a transposed
+//     copy of the router weight ([E][H], so that one expert's weights are
+//     contiguous);
+//  2. route_exact_kernel -- per token, bounds the gap between estimate and
+//     canonical logit, keeps the experts that the bound cannot exclude from
+//     the top K, evaluates only their canonical fma chains, and selects among
+//     them.
+//
+// Why the result is identical to evaluating every canonical logit.  For one
+// token write p_h = x_h w_he (exact in float32: bf16 x bf16), B_e = sum |p_h|,
+// u = 2^-24, L_e the canonical logit and A_e the estimate plus bias.
+//   * The canonical chain rounds once per step: |L_e - (S_e + b_e)| <=
+//     gamma_H B_e + u |L_e|, gamma_H = H u / (1 - H u) (recursive summation).
+//   * One v_mfma adds 16 exact products to its accumulator.  Even an adder
+//     that aligned all 17 terms to the largest one without guard bits would
+//     err by at most 36 u times their absolute sum, so H/16 of them, plus at
+//     most 16 float32 additions of slice partials, stay within
+//     (2.25 H + 16) u B_e + u |A_e|.
+//   * Cauchy-Schwarz: B_e <= ||x|| ||w_e||.  The norms come from float32 sums
+//     of squares, whose relative error (below 2 H u) is covered by the factor
+//     (1 + 3 H u).
+// Hence |A_e - L_e| <= D_e = 5 H u ||x|| ||w_e|| (1 + 3 H u) + 2^-21 |A_e| +
+// 1e-30, for H <= 65536.  If K experts f have A_f - D_f >= theta > A_e + D_e
+// then L_f > L_e for each of them and e is outside the top K.  The
+// candidates are the experts with A_e + D_e >= theta, theta = the K-th
+// largest A_f - D_f: at least K of them (those defining theta), including
+// every member of the top K.  Selecting the K best candidates by canonical
+// logit, with the same key and tie rule, reproduces the full selection.
+// ---------------------------------------------------------------------------
+constexpr int kScreenE = 128;   // experts of the screened path
+constexpr int kScrHC = 64;      // h per staged chunk: 128-byte rows of bf16
+constexpr int kScrNB = 4;       // copy-ring stages
+
+// Physical 16-byte slot of logical segment c of row r in a tile of 128-byte
+// rows (XOR is its own inverse, so the same map gives the logical segment of a
+// physical slot).  The 16 rows one ds_read_b128 pass reads at one segment land
+// on 16 distinct 4-bank groups.
+__device__ __forceinline__ int swz128(int r, int c) { return c ^ ((r >> 1) & 7); }
+// 256-byte rows (one h of the router weight, 128 experts): rows h and h + 8,
+// read together by one B fragment, put a 64-byte expert group on different banks.
+__device__ __forceinline__ int swz256(int h, int c) { return c ^ (((h >> 3) & 3) << 2); }
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Slices of H for the screening kernel: enough workgroups to cover the chip,
+// every slice a whole number of chunks.
+__host__ __device__ inline int screen_tokens_per_block(int T) { return T >= 2048 ? 64 : 32; }
+inline int screen_slices(int T, int H) {
+    const int nblk = (T + screen_tokens_per_block(T) - 1) / screen_tokens_per_block(T);
+    const int chunks = H / kScrHC;
+    int S = 1;
+    while (nblk * S < 256 && S < 16 && chunks % (2 * S) == 0) S *= 2;
+    return S;
+}
+
+struct ScreenWs {
+    uint16_t* wT;   // [E][H] bf16
+    float* part;    // [S][T][E] estimate partial sums
+    float* nx;      // [S][T] partial squared norms of token rows
+    float* nw;      // [S][E] partial squared norms of router-weight columns
+    size_t bytes;
+};
+
+inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+inline ScreenWs screen_layout(const moe_shape& s, void* base) {
+    const int S = screen_slices(s.T, s.H);
+    ScreenWs w{};
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t n) { char* q = p ? p + off : nullptr; off += align256(n); return q; };
+    w.wT = reinterpret_cast<uint16_t*>(take(static_cast<size_t>(s.E) * s.H * 2));
+    w.part = reinterpret_cast<float*>(take(static_cast<size_t>(S) * s.T * s.E * 4));
+    w.nx = reinterpret_cast<float*>(take(static_cast<size_t>(S) * s.T * 4));
+    w.nw = reinterpret_cast<float*>(take(static_cast<size_t>(S) * s.E * 4));
+    w.bytes = off;
+    return w;
+}
+
+template <int TM>   // 32-token MFMA tiles per workgroup
+__global__ __launch_bounds__(256) void route_screen_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int H, int Hs, int nblk,
+    uint16_t* __restrict__ wT, float* __restrict__ part, float* __restrict__ nx, float* __restrict__ nw) {
+    constexpr int E = kScreenE;
+    constexpr int BT = 32 * TM;
+    constexpr int XSTAGE = BT * kScrHC;              // elements: BT rows of 64 h
+    constexpr int WSTAGE = kScrHC * E;               // 64 rows of 128 experts
+    constexpr int STAGE = XSTAGE + WSTAGE;
+    constexpr int XI = XSTAGE / 512;                 // 1 KiB copies per stage (8 x rows each)
+    constexpr int WI = WSTAGE / 512;                 // (4 weight rows each)
+    constexpr int Q = (XI + WI) / 4;                 // copies per wave per stage
+    static_assert((XI + WI) % 4 == 0, "copies must split evenly over the four waves");
+    __shared__ __attribute__((aligned(1024))) uint16_t s_ring[kScrNB][STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int blk = blockIdx.x, sl = blockIdx.y;
+    const int tok0 = blk * BT;
+    const int hbeg = sl * Hs;
+    const int nc = Hs / kScrHC;
+
+    // this lane's source for chunk 0, the per-chunk stride, and the wave-uniform
+    // LDS offset of each of the wave's copies
+    const uint16_t* src[Q];
+    int stride[Q], dst[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int ins = wave * Q + q;
+        if (ins < XI) {
+            const int r = ins * 8 + (lane >> 3);
+            const int t = min(tok0 + r, T - 1);
+            src[q] = x + static_cast<int64_t>(t) * H + hbeg + swz128(r, lane & 7) * 8;
+            stride[q] = kScrHC;
+            dst[q] = ins * 512;
+        } else {
+            const int j = ins - XI;
+            const int h = j * 4 + (lane >> 4);
+            src[q] = w + static_cast<int64_t>(hbeg + h) * E + swz256(h, lane & 15) * 8;
+            stride[q] = kScrHC * E;
+            dst[q] = XSTAGE + j * 512;
+        }
+    }
+    auto issue = [&](int kc, int st) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) dma16(src[q] + static_cast<int64_t>(kc) * stride[q], &s_ring[st][dst[q]]);
+    };
+
+    floatx16 acc[TM];
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[m][v] = 0.0f;
+    float nxp[TM];
+#pragma unroll
+    for (int m = 0; m < TM; ++m) nxp[m] = 0.0f;
+    float nwp = 0.0f;
+
+    const int col = lane & 31;            // B column / A row within a 32 tile
+    const int kg = lane >> 5;             // which 8 of the 16 k of a step
+    const int e = wave * 32 + col;        // this lane's expert (B operand)
+
+    auto compute = [&](int st, int kc) {
+        const uint16_t* sx = s_ring[st];
+        const uint16_t* sw = s_ring[st] + XSTAGE;
+        const bool write_t = ((hbeg / kScrHC + kc) % nblk) == blk;   // this block stores this chunk of wT
+#pragma unroll
+        for (int ks = 0; ks < kScrHC / 16; ++ks) {
+            // B fragment: 8 consecutive h of expert e
+            uint32_t b32[4];
+#pragma unroll
+            for (int j2 = 0; j2 < 4; ++j2) {
+                uint32_t pr = 0;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int h = ks * 16 + kg * 8 + j2 * 2 + hf;
+                    const uint32_t v = sw[h * E + swz256(h, e >> 3) * 8 + (e & 7)];
+                    pr |= v << (16 * hf);
+                }
+                b32[j2] = pr;
+            }
+            u32x4 b = {b32[0], b32[1], b32[2], b32[3]};
+#pragma unroll
+            for (int j2 = 0; j2 < 4; ++j2) {
+                const float lo = bf_lo(b32[j2]), hi = bf_hi(b32[j2]);
+                nwp = fmaf(lo, lo, nwp);
+                nwp = fmaf(hi, hi, nwp);
+            }
+            if (write_t)
+                *reinterpret_cast<u32x4*>(wT + static_cast<int64_t>(e) * H + hbeg + kc * kScrHC + ks * 16 + kg * 8) = b;
+#pragma unroll
+            for (int m = 0; m < TM; ++m) {
+                const int r = m * 32 + col;
+                const u32x4 a = *reinterpret_cast<const u32x4*>(&sx[r * kScrHC + swz128(r, ks * 2 + kg) * 8]);
+                if (wave == 0) {
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2) {
+                        const float lo = bf_lo(a[j2]), hi = bf_hi(a[j2]);
+                        nxp[m] = fmaf(lo, lo, nxp[m]);
+                        nxp[m] = fmaf(hi, hi, nxp[m]);
+                    }
+                }
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                 __builtin_bit_cast(bf16x8_t, b), acc[m], 0, 0, 0);
+            }
+        }
+    };
+
+    // ring: chunk kc lives in stage kc % NB; NB-1 chunks in flight (indices past
+    // the end are clamped: harmless reloads into stages already consumed)
+#pragma unroll
+    for (int q = 0; q < kScrNB - 1; ++q) issue(min(q, nc - 1), q);
+    for (int kc = 0; kc < nc; ++kc) {
+        wait_vmcnt<Q * (kScrNB - 2)>();     // this wave's copies of chunk kc have landed
+        __builtin_amdgcn_s_barrier();       // ... everyone's, and stage (kc - 1) is free
+        issue(min(kc + kScrNB - 1, nc - 1), (kc + kScrNB - 1) % kScrNB);
+        compute(kc % kScrNB, kc);
+    }
+    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is released
+
+    // estimates: lane holds column e and rows 8*(v/4) + 4*kg + v%4 of each 32-row tile
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int t = tok0 + m * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+            if (t < T) part[(static_cast<int64_t>(sl) * T + t) * E + e] = acc[m][v];
+        }
+    if (wave == 0) {
+#pragma unroll
+        for (int m = 0; m < TM; ++m) {
+            const float n2 = nxp[m] + __shfl_xor(nxp[m], 32, kWave);
+            const int t = tok0 + m * 32 + col;
+            if (kg == 0 && t < T) nx[static_cast<int64_t>(sl) * T + t] = n2;
+        }
+    }
+    if (blk == 0) {
+        const float n2 = nwp + __shfl_xor(nwp, 32, kWave);
+        if (kg == 0) nw[sl * E + e] = n2;
+    }
+}
+
+__device__ __forceinline__ uint64_t group16_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+        uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 16);
+        uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 16);
+        uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// 256-byte rows (128 bf16): the 16 rows one ds_read_b128 pass reads at one
+// segment land on 16 distinct 4-bank groups.
+__device__ __forceinline__ int swz256r(int r, int c) { return c ^ (r & 15); }
+
+// A workgroup owns BT = 4 * WAVES tokens; 16 lanes per token.  Lane s of a
+// token's group screens experts s, s+16, ..., s+112, then evaluates candidates
+// s, s+16, ... of the token's candidate list.  The canonical chains read
+// 128-h chunks of the transposed router-weight rows of the union of the
+// block's candidates and of the token rows, staged in LDS by a ring of
+// direct-to-LDS copies (NB stages); each wave widens its four token rows to
+// float32 once per chunk in a wave-private area, so a chain step costs one
+// widening of the weight and one fma.
+template <int WAVES, int NB, int SMAX>
+__global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wT, const float* __restrict__ bias,
+    const float* __restrict__ part, const float* __restrict__ nx, const float* __restrict__ nw,
+    int T, int H, int K, int S, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    constexpr int E = kScreenE;
+    constexpr int NT = WAVES * 64;
+    constexpr int BT = 4 * WAVES;
+    constexpr int HC = 128;                                 // h per chunk: 256-byte bf16 rows
+    constexpr int RE = HC;                                  // elements per staged row
+    constexpr int TROWS = BT < 4 ? 4 : BT;                  // token rows (a copy moves 4 rows)
+    constexpr int XOFF = E * RE;                            // element offset of the token rows
+    constexpr int SPARE = XOFF + TROWS * RE;                // 1 KiB target of padding copies
+    constexpr int STAGE = SPARE + 512;                      // elements
+    constexpr int QMAX = (E / 4 + TROWS / 4 + WAVES - 1) / WAVES;   // copies per wave per chunk, at most
+    __shared__ __attribute__((aligned(1024))) uint16_t s_ring[NB][STAGE];
+    __shared__ __attribute__((aligned(16))) float s_xf[WAVES][4][HC + 4];
+    __shared__ uint8_t s_cand[WAVES][4][E];
+    __shared__ int s_flag[E];
+    __shared__ uint8_t s_map[E];
+    __shared__ uint8_t s_list[E];
+    __shared__ int s_nu;
+    __shared__ float s_nw[E];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, s = lane & 15;
+    const int tl = wave * 4 + g;                 // token within the block
+    const int tok0 = blockIdx.x * BT;
+    const int t = tok0 + tl;
+    const bool valid = t < T;
+    const float Hu = static_cast<float>(H) * 0x1p-24f;
+
+    // squared norms of the router-weight columns (sum of the slice partials, once per workgroup)
+    for (int i = tid; i < E; i += NT) {
+        s_flag[i] = 0;
+        float n2 = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < SMAX; ++sl)
+            if (sl < S) n2 += nw[sl * E + i];
+        s_nw[i] = n2;
+    }
+    __syncthreads();
+
+    // ---- screen: estimates, windows, theta, candidates ----
+    // all slice partials of this lane's 8 experts are loaded before any is summed
+    float pv[SMAX][8];
+    float nxv[SMAX];
+#pragma unroll
+    for (int sl = 0; sl < SMAX; ++sl) {
+        nxv[sl] = (valid && sl < S) ? nx[static_cast<int64_t>(sl) * T + t] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            pv[sl][i] = (valid && sl < S) ? part[(static_cast<int64_t>(sl) * T + t) * E + s + 16 * i] : 0.0f;
+    }
+    float nxs = 0.0f;
+#pragma unroll
+    for (int sl = 0; sl < SMAX; ++sl) nxs += nxv[sl];
+    const float sx = sqrtf(nxs) * (1.0f + 3.0f * Hu);
+    float hi[8];
+    uint64_t klo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = s + 16 * i;
+        float a = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < SMAX; ++sl) a += pv[sl][i];
+        const float la = bias != nullptr ? a + bias[e] : a;
+        const float d = 5.0f * Hu * (sx * sqrtf(s_nw[e])) + 0x1p-21f * fabsf(la) + 1e-30f;
+        hi[i] = valid ? la + d : -INFINITY;
+        klo[i] = make_key(valid ? la - d : -INFINITY, e);
+    }
+    uint64_t kth = 0ull;
+    {
+        uint32_t taken = 0u;
+        for (int r = 0; r < K; ++r) {
+            uint64_t best = 0ull;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) best = (!((taken >> i) & 1u) && klo[i] > best) ? klo[i] : best;
+            best = group16_max_u64(best);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (klo[i] == best) taken |= 1u << i;
+            kth = best;
+        }
+    }
+    const float theta = key_logit(kth);
+    uint32_t cm = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (valid && hi[i] >= theta) cm |= 1u << i;
+    const int mine = __builtin_popcount(cm);
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        const int o = __shfl_up(incl, d, 16);
+        if (s >= d) incl += o;
+    }
+    const int total = __shfl(incl, 15, 16);      // candidates of this token
+    {
+        int pos = incl - mine;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if ((cm >> i) & 1u) {
+                s_cand[wave][g][pos++] = static_cast<uint8_t>(s + 16 * i);
+                s_flag[s + 16 * i] = 1;
+            }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const bool f0 = s_flag[lane] != 0, f1 = s_flag[lane + 64] != 0;
+        const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
+        const uint64_t below = (1ull << lane) - 1ull;
+        const int r0 = __popcll(m0 & below);
+        const int r1 = __popcll(m0) + __popcll(m1 & below);
+        if (f0) { s_list[r0] = static_cast<uint8_t>(lane); s_map[lane] = static_cast<uint8_t>(r0); }
+        if (f1) { s_list[r1] = static_cast<uint8_t>(lane + 64); s_map[lane + 64] = static_cast<uint8_t>(r1); }
+        if (lane == 0) s_nu = __popcll(m0) + __popcll(m1);
+    }
+    __syncthreads();
+    const int nu = s_nu;
+
+    // ---- copy plan: ceil(nu/4) copies of union rows and TROWS/4 of token rows
+    // (4 rows of 256 B each), spread evenly over the waves (padding copies go to
+    // the spare KiB) ----
+    const int nU = (nu + 3) >> 2;
+    const int nI = nU + TROWS / 4;
+    const int q = (nI + WAVES - 1) / WAVES;      // uniform over the workgroup
+    const uint16_t* src[QMAX];
+    int dst[QMAX];
+#pragma unroll
+    for (int j = 0; j < QMAX; ++j) {
+        const int ins = wave * q + j;
+        const int slot = lane & 15;
+        if (ins < nU) {
+            const int u = ins * 4 + (lane >> 4);
+            const int ex = s_list[u < nu ? u : 0];
+            src[j] = wT + static_cast<int64_t>(ex) * H + swz256r(u, slot) * 8;
+            dst[j] = ins * 4 * RE;
+        } else if (ins < nI) {
+            const int rr = (ins - nU) * 4 + (lane >> 4);
+            const int tt = min(tok0 + rr, T - 1);
+            src[j] = x + static_cast<int64_t>(tt) * H + slot * 8;
+            dst[j] = XOFF + (ins - nU) * 4 * RE;
+        } else {
+            src[j] = x + static_cast<int64_t>(tok0) * H + slot * 8;
+            dst[j] = SPARE;
+        }
+    }
+    auto issue = [&](int kc, int st) {
+#pragma unroll
+        for (int j = 0; j < QMAX; ++j)
+            if (j < q) dma16(src[j] + static_cast<int64_t>(kc) * HC, &s_ring[st][dst[j]]);
+    };
+
+    // this lane's chains: candidates s + 16 p of its token
+    constexpr int PMAX = E / 16;
+    int urow[PMAX];
+    int eid[PMAX];
+    const int np = valid ? (total - s + 15) / 16 : 0;   // chains of this lane
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int c = s + 16 * p;
+        eid[p] = c < total ? s_cand[wave][g][c] : 0;
+        urow[p] = c < total ? s_map[eid[p]] : 0;
+    }
+    float acc[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) acc[p] = 0.0f;
+    const int nc = H / HC;
+    const float* xw = s_xf[wave][g];
+    const int xrow = XOFF + (wave * 4 + g) * RE;
+
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j) issue(min(j, nc - 1), j);
+    for (int kc = 0; kc < nc; ++kc) {
+        // chunk kc's copies are followed by q * (NB - 2) younger ones (vmcnt holds
+        // at most 63; waiting for fewer than needed is merely stricter)
+        wait_vmcnt_bin<0, 64>(min(q * (NB - 2), 63));
+        __builtin_amdgcn_s_barrier();
+        issue(min(kc + NB - 1, nc - 1), (kc + NB - 1) % NB);
+        const uint16_t* sr = s_ring[kc % NB];
+        // widen this wave's four token rows: lane (g, s) converts elements 8s .. 8s+7
+        {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&sr[xrow + s * 8]);
+            floatx4 lo4 = {bf_lo(v[0]), bf_hi(v[0]), bf_lo(v[1]), bf_hi(v[1])};
+            floatx4 hi4 = {bf_lo(v[2]), bf_hi(v[2]), bf_lo(v[3]), bf_hi(v[3])};
+            *reinterpret_cast<floatx4*>(&s_xf[wave][g][8 * s]) = lo4;
+            *reinterpret_cast<floatx4*>(&s_xf[wave][g][8 * s + 4]) = hi4;
+        }
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p < np) {
+                // operands of segment c + 1 are read while segment c's fma chain runs
+                float a = acc[p];
+                const int u = urow[p];
+                const uint16_t* wr = sr + u * RE;
+                u32x4 wv = *reinterpret_cast<const u32x4*>(&wr[swz256r(u, 0) * 8]);
+                floatx4 x0 = *reinterpret_cast<const floatx4*>(&xw[0]);
+                floatx4 x1 = *reinterpret_cast<const floatx4*>(&xw[4]);
+#pragma unroll
+                for (int c = 0; c < HC / 8; ++c) {
+                    u32x4 wn;
+                    floatx4 y0, y1;
+                    if (c + 1 < HC / 8) {
+                        wn = *reinterpret_cast<const u32x4*>(&wr[swz256r(u, c + 1) * 8]);
+                        y0 = *reinterpret_cast<const floatx4*>(&xw[8 * c + 8]);
+                        y1 = *reinterpret_cast<const floatx4*>(&xw[8 * c + 12]);
+                    }
+                    a = fmaf(x0[0], bf_lo(wv[0]), a);
+                    a = fmaf(x0[1], bf_hi(wv[0]), a);
+                    a = fmaf(x0[2], bf_lo(wv[1]), a);
+                    a = fmaf(x0[3], bf_hi(wv[1]), a);
+                    a = fmaf(x1[0], bf_lo(wv[2]), a);
+                    a = fmaf(x1[1], bf_hi(wv[2]), a);
+                    a = fmaf(x1[2], bf_lo(wv[3]), a);
+                    a = fmaf(x1[3], bf_hi(wv[3]), a);
+                    if (c + 1 < HC / 8) {
+                        wv = wn;
+                        x0 = y0;
+                        x1 = y1;
+                    }
+                }
+                acc[p] = a;
+            }
+        }
+    }
+    wait_vmcnt<0>();
+
+    // ---- select the top K of the candidates by canonical logit ----
+    uint64_t key[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const float l = bias != nullptr ? acc[p] + bias[eid[p]] : acc[p];
+        key[p] = p < np ? make_key(l, eid[p]) : 0ull;
+    }
+    int my_e[4] = {0, 0, 0, 0};
+    float my_l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float l0 = 0.0f, sum = 0.0f;
+    for (int r = 0; r < K; ++r) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) best = key[p] > best ? key[p] : best;
+        best = group16_max_u64(best);
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p)
+            if (key[p] == best) key[p] = 0ull;
+        const float l = key_logit(best);
+        if (r == 0) l0 = l;
+        sum += expf(l - l0);
+        if ((r & 15) == s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((r >> 4) == j) {
+                    my_e[j] = key_expert(best);
+                    my_l[j] = l;
+                }
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = s + 16 * j;
+            if (r < K) {
+                topk_idx[static_cast<int64_t>(t) * K + r] = my_e[j];
+                topk_w[static_cast<int64_t>(t) * K + r] = expf(my_l[j] - l0) / sum;
+            }
+        }
+    }
+}
+
+template <int TM>
+void launch_screen(const moe_shape& s, const uint16_t* x, const uint16_t* w, const ScreenWs& ws, int S,
+                   hipStream_t st) {
+    const int nblk = (s.T + 32 * TM - 1) / (32 * TM);
+    hipLaunchKernelGGL(route_screen_kernel<TM>, dim3(nblk, S), dim3(256), 0, st, x, w, s.T, s.H, s.H / S, nblk,
+                       ws.wT, ws.part, ws.nx, ws.nw);
+}
+
+template <int WAVES, int NB, int SMAX>
+void launch_exact(const moe_shape& s, const uint16_t* x, const float* bias, const ScreenWs& ws, int S,
+                  int32_t* idx, float* tw, hipStream_t st) {
+    const int grid = (s.T + 4 * WAVES - 1) / (4 * WAVES);
+    hipLaunchKernelGGL((route_exact_kernel<WAVES, NB, SMAX>), dim3(grid), dim3(WAVES * 64), 0, st, x, ws.wT, bias,
+                       ws.part, ws.nx, ws.nw, s.T, s.H, s.K, S, idx, tw);
+}
+
+void launch_route_screened(const moe_shape& s, const uint16_t* x, const uint16_t* w, const float* bias,
+                           int32_t* idx, float* tw, void* ws_base, hipStream_t st) {
+    const ScreenWs ws = screen_layout(s, ws_base);
+    const int S = screen_slices(s.T, s.H);
+    if (screen_tokens_per_block(s.T) == 64) launch_screen<2>(s, x, w, ws, S, st);
+    else launch_screen<1>(s, x, w, ws, S, st);
+    // the exact kernel sums SMAX >= S slice partials (screen_slices gives S <= 16)
+    if (s.T >= 2048) {
+        if (S <= 4) launch_exact<8, 3, 4>(s, x, bias, ws, S, idx, tw, st);
+        else launch_exact<8, 3, 16>(s, x, bias, ws, S, idx, tw, st);
+    } else {
+        launch_exact<4, 3, 16>(s, x, bias, ws, S, idx, tw, st);
+    }
+}
+
+// The exact kernel walks H in whole 128-element chunks (H % 128 == 0); the
+// error bound holds for H <= 65536.  Below 512 tokens there are too few
+// candidate chains to fill the chip and each one is a dependent sequence of
+// H fma, so evaluating every logit directly is as fast.
+constexpr int kScreenMinTokens = 512;
+bool screen_eligible(const moe_shape& s, int x_dtype, int w_dtype) {
+    return x_dtype == MOE_BF16 && w_dtype == MOE_BF16 && s.E == kScreenE && s.T >= kScreenMinTokens &&
+           s.H % 128 == 0 && s.H <= 65536;
+}
+
 }  // namespace
 
+size_t route_screen_bytes(const moe_shape& s, int x_dtype, int w_dtype) {
+    return screen_eligible(s, x_dtype, w_dtype) ? screen_layout(s, nullptr).bytes : 0;
+}
+
 int launch_route(const moe_shape& s, const void* x, int x_dtype, const void* w, const float* bias,
-                 int32_t* topk_idx, float* topk_w, float* logits, hipStream_t st) {
-    if (x_dtype == MOE_BF16)
+                 int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes, hipStream_t st) {
+    const size_t need = route_screen_bytes(s, x_dtype, x_dtype);
+    if (logits == nullptr && ws != nullptr && need > 0 && ws_bytes >= need)
+        launch_route_screened(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias, topk_idx,
+                              topk_w, ws, st);
+    else if (x_dtype == MOE_BF16)
         launch_route_dt<uint16_t>(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
                                   topk_idx, topk_w, logits, st);
     else

@@ -62,7 +62,8 @@ def test_invalid_shapes(kw, status):
     lib = B.load()
     s = _shape(**kw).c()
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
-    assert lib.moe_route(ctypes.byref(s), fake, B.MOE_BF16, fake, B.MOE_BF16, None, fake, fake, None, None) == status
+    assert lib.moe_route(ctypes.byref(s), fake, B.MOE_BF16, fake, B.MOE_BF16, None, fake, fake, None, None, 0,
+                         None) == status
     assert lib.moe_combine(ctypes.byref(s), fake, B.MOE_BF16, fake, fake, fake, None) == status
     assert lib.moe_layer_workspace_bytes(ctypes.byref(s)) == 0
     assert lib.moe_packed_weight_bytes(ctypes.byref(s)) == 0
@@ -74,10 +75,24 @@ def test_invalid_pointers_and_enums():
     p16 = ctypes.c_void_p(0x1000)
     odd = ctypes.c_void_p(0x1002)
     S = ctypes.byref(s)
-    assert lib.moe_route(S, None, B.MOE_BF16, p16, B.MOE_BF16, None, p16, p16, None, None) == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(S, odd, B.MOE_BF16, p16, B.MOE_BF16, None, p16, p16, None, None) == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(S, p16, B.MOE_BF16, p16, B.MOE_F32, None, p16, p16, None, None) == B.MOE_ERR_UNSUPPORTED
-    assert lib.moe_route(S, p16, 7, p16, 7, None, p16, p16, None, None) == B.MOE_ERR_UNSUPPORTED
+    R = lib.moe_route
+    assert R(S, None, B.MOE_BF16, p16, B.MOE_BF16, None, p16, p16, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert R(S, odd, B.MOE_BF16, p16, B.MOE_BF16, None, p16, p16, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert R(S, p16, B.MOE_BF16, p16, B.MOE_F32, None, p16, p16, None, None, 0, None) == B.MOE_ERR_UNSUPPORTED
+    assert R(S, p16, 7, p16, 7, None, p16, p16, None, None, 0, None) == B.MOE_ERR_UNSUPPORTED
+    # the screened router's workspace: 128 experts, bf16
+    s128 = _shape(T=1000, E=128, K=8, e_end=32).c()
+    S128 = ctypes.byref(s128)
+    rneed = lib.moe_route_workspace_bytes(S128)
+    assert rneed > 0
+    assert R(S128, p16, B.MOE_BF16, p16, B.MOE_BF16, None, p16, p16, None, p16, rneed - 1,
+             None) == B.MOE_ERR_WORKSPACE
+    assert R(S128, p16, B.MOE_BF16, p16, B.MOE_BF16, None, p16, p16, None, odd, rneed,
+             None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_workspace_bytes(S) == 0            # 8 experts: no screened path
+    s192 = _shape(T=1000, E=128, K=8, e_end=32, H=192).c()
+    assert lib.moe_route_workspace_bytes(ctypes.byref(s192)) == 0   # H not a multiple of 128
+    assert lib.moe_layer_workspace_bytes(S128) >= rneed
     G = lib.moe_grouped_gemm
     assert G(S, p16, B.MOE_BF16, None, p16, p16, 5, 0, p16, B.MOE_BF16, None) == B.MOE_ERR_INVALID_ARG
     assert G(S, p16, B.MOE_F16, None, p16, p16, B.MOE_GEMM_DOWN, B.MOE_EPI_SWIGLU, p16, B.MOE_BF16,

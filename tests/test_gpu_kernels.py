@@ -81,6 +81,70 @@ def test_route_exact_ties(B):
     assert np.all(lg0 == 0) and np.array_equal(idx0, np.tile(np.arange(4), (70, 1))) and np.all(tw0 == 0.25)
 
 
+def _screened(B, x, w, K, bias=None):
+    """Screened route (MFMA estimates + canonical chains for the candidates) and the full canonical route."""
+    T, H = x.shape
+    E = w.shape[1]
+    s = B.Shape(T, H, E, K, 64, 0, E)
+    assert B.moe_route_workspace_bytes(s) > 0
+    xt, wt = to_torch(x), to_torch(w)
+    bt = to_torch(bias) if bias is not None else None
+    idx, tw, _ = B.moe_route(s, xt, wt, bt)
+    idx_c, tw_c, _ = B.moe_route(s, xt, wt, bt, screened=False)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), tw.cpu().numpy(), idx_c.cpu().numpy(), tw_c.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,K,seed", [(512, 128, 1, 0), (513, 128, 8, 1), (1029, 128, 8, 2), (777, 512, 8, 3),
+                                        (700, 4096, 8, 4), (2050, 256, 8, 5), (600, 1024, 64, 6),
+                                        (3000, 4096, 8, 9), (6000, 4096, 8, 7)])
+def test_route_screened_bit_exact(B, T, H, K, seed):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.standard_normal((T, H), dtype=np.float32))
+    w = _bf16(rng.standard_normal((H, 128), dtype=np.float32) * np.float32(0.02))
+    idx, tw, idx_c, tw_c = _screened(B, x, w, K)
+    ri, rw, _ = oracle.route(W.as_f32(x), W.as_f32(w), None, K)
+    assert np.array_equal(idx, ri)
+    assert np.array_equal(idx, idx_c)
+    assert np.abs(tw - rw).max() <= 1e-6
+    assert np.abs(tw - tw_c).max() <= 1e-6
+
+
+def test_route_screened_bias_ties_and_degenerate(B):
+    # skewed bias
+    wl = W.WORKLOADS["skewed_prefill"].replace(T=1500, H=512)
+    rng = np.random.default_rng(8)
+    x = _bf16(rng.standard_normal((wl.T, wl.H), dtype=np.float32))
+    w = _bf16(rng.standard_normal((wl.H, 128), dtype=np.float32) * np.float32(0.02))
+    bias = W.gen_bias(wl)
+    idx, tw, idx_c, _ = _screened(B, x, w, 8, bias)
+    ri, rw, _ = oracle.route(W.as_f32(x), W.as_f32(w), bias, 8)
+    assert np.array_equal(idx, ri) and np.array_equal(idx, idx_c) and np.abs(tw - rw).max() <= 1e-6
+    # bitwise ties: experts 64.. copy experts 0..63 (equal estimates and equal canonical logits)
+    w2 = w[:256].copy()
+    w2[:, 64:] = w2[:, :64]
+    x2 = x[:600, :256].copy()
+    idx, tw, idx_c, _ = _screened(B, x2, w2, 8)
+    ri, rw, _ = oracle.route(W.as_f32(x2), W.as_f32(w2), None, 8)
+    assert np.array_equal(idx, ri) and np.array_equal(idx, idx_c) and np.abs(tw - rw).max() <= 1e-6
+    # zero router: no estimate error, every expert a candidate; experts 0..K-1, weights 1/K
+    idx, tw, _, _ = _screened(B, x[:577, :128].copy(), np.zeros((128, 128), np.uint16), 8)
+    assert np.array_equal(idx, np.tile(np.arange(8), (577, 1))) and np.all(tw == np.float32(0.125))
+    # H not a multiple of 128, or fewer than 512 tokens: no screened path (no workspace)
+    assert B.moe_route_workspace_bytes(B.Shape(600, 192, 128, 8, 64, 0, 128)) == 0
+    assert B.moe_route_workspace_bytes(B.Shape(511, 256, 128, 8, 64, 0, 128)) == 0
+    idx, tw, lg = B.moe_route(B.Shape(600, 192, 128, 8, 64, 0, 128), to_torch(x[:600, :192].copy()),
+                              to_torch(w[:192].copy()))
+    torch.cuda.synchronize()
+    ri, rw, _ = oracle.route(W.as_f32(x[:600, :192]), W.as_f32(w[:192]), None, 8)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    # large activations (products still exact), K = 1
+    x3 = _bf16(W.as_f32(x[:640]) * np.float32(64.0))
+    idx, tw, idx_c, _ = _screened(B, x3, w, 1)
+    ri, rw, _ = oracle.route(W.as_f32(x3), W.as_f32(w), None, 1)
+    assert np.array_equal(idx, ri) and np.all(tw == 1.0)
+
+
 @pytest.mark.parametrize("E,K", [(128, 8), (8, 2), (300, 16), (1024, 64)])
 def test_route_from_logits_ties(B, E, K):
     T = 257
