@@ -37,7 +37,10 @@
 //   * persistent workgroups walk a tile list laid out per expert as
 //     [n-tile][m-tile], so workgroups that run together share one weight
 //     tile; tile ids are split into one contiguous range per XCD (workgroup b
-//     runs on XCD b % 8), keeping those sharers inside one L2;
+//     runs on XCD b % 8), keeping those sharers inside one L2; an expert's
+//     rows are split into m-tiles of equal height, so the sharers do equal
+//     work and stay in step, and MFMAs of 32-row groups past the segment are
+//     skipped;
 //   * m-tiles per expert come from the device-side offsets (no host sync);
 //   * epilogues: plain store (float32, bf16 or fp16), or SwiGLU for the
 //     gate/up problem, whose weights are packed so that each 64-column block
@@ -151,8 +154,6 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E_loc
     __syncthreads();
 }
 
-// Wait until at most N vector-memory operations of this wave are in flight
-// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
 template <int WN, int MODE, bool F16, int OUT, int NB>
 __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
     typedef typename OutType<OUT>::type OutT;
@@ -204,10 +205,16 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
         const int n_tile = local / mt_e;
         const int m_unit = local - n_tile * mt_e;
         const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
-        const int row0 = seg0 + m_unit * UM;
-        const int rows_valid = min(UM, seg1 - row0);
+        // the expert's rows are split into mt_e tiles of equal height (a multiple
+        // of 32, at most UM), so the tiles that share one weight tile do equal
+        // work and stream it through L2 together
+        const int um = min(UM, ((seg1 - seg0 + mt_e - 1) / mt_e + 31) & ~31);
+        const int row0 = seg0 + m_unit * um;
+        const int rows_valid = min(um, seg1 - row0);
+        if (rows_valid <= 0) continue;                  // uniform: the whole workgroup skips
         const int my_rows = rows_valid - mh * BM;      // rows of this wave's half (<= 0: idle half)
         const bool active = my_rows > 0;
+        const int na = min(TM, (my_rows + 31) >> 5);   // 32-row MFMA tiles holding valid rows
 
         // A copies of this thread: LDS granule slot (i * NWAVES + wave) * 64 + lane holds
         // swizzled position (row, g'); the swizzle is an involution, so the logical
@@ -246,7 +253,8 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
             const int kg = ks * 2 + (lane >> 5);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                fa[i] = *reinterpret_cast<const u32x4*>(&s_a[st][lds_off(mh * BM + i * 32 + (lane & 31), kg)]);
+                if (i < na)
+                    fa[i] = *reinterpret_cast<const u32x4*>(&s_a[st][lds_off(mh * BM + i * 32 + (lane & 31), kg)]);
             fb[0] = *reinterpret_cast<const u32x4*>(&s_b[st][nq][2 * ks][lane * 8]);
             fb[1] = *reinterpret_cast<const u32x4*>(&s_b[st][nq][2 * ks + 1][lane * 8]);
         };
@@ -266,11 +274,14 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 
         u32x4 fa_cur[TM], fb_cur[2], fa_nxt[TM], fb_nxt[2];
         static_assert(KS == 2, "the stage schedule below is written for two k-steps");
+        // 32-row groups past the segment are skipped (wave-uniform branch)
         auto mfmas = [&](const u32x4 (&fa)[TM], const u32x4 (&fb)[2]) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                acc[i][0] = mfma32<F16>(fa[i], fb[0], acc[i][0]);
-                acc[i][1] = mfma32<F16>(fa[i], fb[1], acc[i][1]);
+                if (i < na) {
+                    acc[i][0] = mfma32<F16>(fa[i], fb[0], acc[i][0]);
+                    acc[i][1] = mfma32<F16>(fa[i], fb[1], acc[i][1]);
+                }
             }
         };
         // One k-tile from ring stage st, entered with its first k-step's fragments
