@@ -76,6 +76,7 @@ struct GemmArgs {
     int Kd;                    // reduction length
     int ldc;                   // output row stride (elements)
     int I;                     // intermediate size (gate/up column remap)
+    int skinny;                // few rows per expert expected: weight-streaming kernel
 };
 
 __device__ __forceinline__ int swz(int row, int kg) {
@@ -347,6 +348,125 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Few rows per expert (decode): the weights dominate the traffic, so each
+// weight byte is read once and applied to all of the expert's rows.  A
+// workgroup owns one (expert, 64-column block) unit; its four waves split the
+// reduction into quarters and stream their weight fragments straight from the
+// fragment-packed weights into a register ring BD k-steps deep, together with
+// the matching fragments of up to 64 rows (two 32-row MFMA tiles; an expert
+// with more rows is handled in further 64-row groups).  The four partial
+// tiles are added in wave order through LDS by all threads, which then apply
+// the epilogue.
+// ---------------------------------------------------------------------------
+template <int MODE, bool F16, int OUT, int BD>
+__global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p) {
+    typedef typename OutType<OUT>::type OutT;
+    constexpr int MT = 2;                              // 32-row tiles per row group
+    __shared__ __attribute__((aligned(16))) float s_red[4][MT][2][16][64];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nblk = p.N >> 6;
+    const int e = blockIdx.x / nblk;
+    const int nb = blockIdx.x - e * nblk;
+    const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
+    const int rows = seg1 - seg0;
+    if (rows <= 0) return;                             // uniform over the workgroup
+
+    const int nks = p.Kd >> 4;                         // k-steps (a multiple of 4)
+    const int kq = nks >> 2;                           // k-steps of this wave
+    const int k0 = wave * kq;
+    const int kblocks = nks;
+    const uint16_t* b_src[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+        b_src[s2] = p.b + ((static_cast<int64_t>(e) * (p.N >> 5) + nb * 2 + s2) * kblocks + k0) * kFragElems +
+                    lane * 8;
+
+    for (int g0 = 0; g0 < rows; g0 += 32 * MT) {
+        const uint16_t* a_src[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const int rr = g0 + t * 32 + (lane & 31);
+            const int r = seg0 + (rr < rows ? rr : 0);
+            const int64_t src = p.a_rows != nullptr ? p.a_rows[r] : r;
+            a_src[t] = p.a + src * p.Kd + static_cast<int64_t>(k0) * 16 + (lane >> 5) * 8;
+        }
+        floatx16 acc[MT][2];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[t][j][v] = 0.0f;
+
+        u32x4 fb[BD][2], fa[BD][MT];
+        auto load = [&](int slot, int kk) {       // k-step kk of this wave's range (clamped)
+            const int kc = min(kk, kq - 1);
+            fb[slot][0] = *reinterpret_cast<const u32x4*>(b_src[0] + static_cast<int64_t>(kc) * kFragElems);
+            fb[slot][1] = *reinterpret_cast<const u32x4*>(b_src[1] + static_cast<int64_t>(kc) * kFragElems);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) fa[slot][t] = *reinterpret_cast<const u32x4*>(a_src[t] + kc * 16);
+        };
+#pragma unroll
+        for (int j = 0; j < BD; ++j) load(j, j);
+        for (int kb = 0; kb < kq; kb += BD) {
+#pragma unroll
+            for (int j = 0; j < BD; ++j) {
+                if (kb + j < kq) {                     // uniform
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        acc[t][0] = mfma32<F16>(fa[j][t], fb[j][0], acc[t][0]);
+                        acc[t][1] = mfma32<F16>(fa[j][t], fb[j][1], acc[t][1]);
+                    }
+                    load(j, kb + j + BD);
+                }
+            }
+        }
+
+        // the four partial tiles go through LDS; each thread then adds the four
+        // partials of 8 (row, column) pairs in wave order and applies the epilogue
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s_red[wave][t][j][v][lane] = acc[t][j][v];
+        __syncthreads();
+        {
+            OutT* __restrict__ C = static_cast<OutT*>(p.c);
+            const int pc0 = nb * 64;
+#pragma unroll 2
+            for (int i = 0; i < MT * 16 * 64 / 256; ++i) {
+                const int idx = static_cast<int>(threadIdx.x) + i * 256;
+                const int ln = idx & 63, v = (idx >> 6) & 15, t = idx >> 10;
+                const int r = g0 + t * 32 + 8 * (v >> 2) + 4 * (ln >> 5) + (v & 3);
+                float g = s_red[0][t][0][v][ln], u = s_red[0][t][1][v][ln];
+#pragma unroll
+                for (int w = 1; w < 4; ++w) {
+                    g += s_red[w][t][0][v][ln];
+                    u += s_red[w][t][1][v][ln];
+                }
+                if (r < rows) {
+                    OutT* crow = C + static_cast<int64_t>(seg0 + r) * p.ldc;
+                    if constexpr (MODE == kSwiGLU) {
+                        store_out<OUT>(crow + (pc0 >> 1) + (ln & 31), silu(g) * u);
+                    } else if constexpr (MODE == kGateUpPlain) {
+                        const int q = pc0 >> 6, wc = ln & 31;
+                        store_out<OUT>(crow + q * 32 + wc, g);
+                        store_out<OUT>(crow + p.I + q * 32 + wc, u);
+                    } else {
+                        store_out<OUT>(crow + pc0 + (ln & 31), g);
+                        store_out<OUT>(crow + pc0 + 32 + (ln & 31), u);
+                    }
+                }
+            }
+        }
+        __syncthreads();                               // s_red reuse by the next row group
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Weight packing into MFMA fragment order.
 // Source [E_loc][Kd][Cs] row-major (y = x W: k is the row, the output column c
 // the column).  Output column c maps to packed column pcol(c): identity for
@@ -407,7 +527,17 @@ int launch_gemm_t(const GemmArgs& args, int max_rows, hipStream_t st) {
 }
 
 template <int MODE, bool F16, int OUT>
+int launch_skinny(const GemmArgs& args, hipStream_t st) {
+    const int64_t grid = static_cast<int64_t>(args.E_loc) * (args.N / 64);
+    hipLaunchKernelGGL((grouped_gemm_skinny_kernel<MODE, F16, OUT, 4>), dim3(static_cast<unsigned>(grid)), dim3(256),
+                       0, st, args);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+template <int MODE, bool F16, int OUT>
 int launch_nw(const GemmArgs& args, int max_rows, hipStream_t st) {
+    if (args.skinny) return launch_skinny<MODE, F16, OUT>(args, st);
     if (args.N % 256 == 0) return launch_gemm_t<4, MODE, F16, OUT>(args, max_rows, st);
     if (args.N % 128 == 0) return launch_gemm_t<2, MODE, F16, OUT>(args, max_rows, st);
     return launch_gemm_t<1, MODE, F16, OUT>(args, max_rows, st);
@@ -468,6 +598,9 @@ int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, cons
     args.c = c;
     args.E_loc = E_loc;
     args.I = s.I;
+    // routed evenly, an expert receives T*K/E rows; at most 64 expected -> the
+    // weight-streaming kernel (it stays correct for any row count)
+    args.skinny = static_cast<int64_t>(s.T) * s.K <= static_cast<int64_t>(64) * s.E;
     if (which == MOE_GEMM_GATE_UP) {
         args.b = packed;
         args.N = 2 * s.I;

@@ -209,7 +209,11 @@ def _gemm_case(B, counts, H, I, seed=7):
 
 @pytest.mark.parametrize("wdt", ["bf16", "f32"])
 @pytest.mark.parametrize("counts,H,I", [([37, 0, 300, 129], 256, 128), ([1], 64, 64), ([128, 128], 128, 192),
-                                        ([0, 0, 5], 192, 64)])
+                                        ([0, 0, 5], 192, 64),
+                                        # few rows per expert on average: the weight-streaming kernel, with
+                                        # experts of 0, 1, 31, 33, 64, 65 and 150 rows (row groups of 64)
+                                        ([150, 0, 1, 31, 33, 0, 0, 64, 65, 0, 0, 0, 0, 0, 0, 0] + [0] * 16,
+                                         256, 128)])
 def test_grouped_gemm_exact_integers(B, counts, H, I, wdt):
     """Both problems on integer-grid operands, float32 output: bit-exact in any order.
     bf16 weights multiply in bf16, float32 weights in fp16; down always in fp16."""
