@@ -435,7 +435,7 @@ void launch_route_dt(const moe_shape& s, const XT* x, const XT* w, const float* 
 // ---------------------------------------------------------------------------
 constexpr int kScreenE = 128;   // experts of the screened path
 constexpr int kScrHC = 64;      // h per staged chunk: 128-byte rows of bf16
-constexpr int kScrNB = 4;       // copy-ring stages
+constexpr int kScrNB = 3;       // copy-ring stages (two chunks in flight; two workgroups fit a CU)
 
 // Physical 16-byte slot of logical segment c of row r in a tile of 128-byte
 // rows (XOR is its own inverse, so the same map gives the logical segment of a
@@ -498,6 +498,8 @@ __global__ __launch_bounds__(256) void route_screen_kernel(
     constexpr int Q = (XI + WI) / 4;                 // copies per wave per stage
     static_assert((XI + WI) % 4 == 0, "copies must split evenly over the four waves");
     __shared__ __attribute__((aligned(1024))) uint16_t s_ring[kScrNB][STAGE];
+    __shared__ float s_nx[4][BT];
+    static_assert(kScrHC / 16 == 4, "one k-step of token norms per wave");
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(256) void route_screen_kernel(
             for (int m = 0; m < TM; ++m) {
                 const int r = m * 32 + col;
                 const u32x4 a = *reinterpret_cast<const u32x4*>(&sx[r * kScrHC + swz128(r, ks * 2 + kg) * 8]);
-                if (wave == 0) {
+                if (wave == ks) {                        // token norms: wave w takes k-step w
 #pragma unroll
                     for (int j2 = 0; j2 < 4; ++j2) {
                         const float lo = bf_lo(a[j2]), hi = bf_hi(a[j2]);
@@ -613,11 +615,19 @@ __global__ __launch_bounds__(256) void route_screen_kernel(
             const int t = tok0 + m * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
             if (t < T) part[(static_cast<int64_t>(sl) * T + t) * E + e] = acc[m][v];
         }
+    // token norms: the four waves' partials (k-steps 0..3 of every chunk), added in wave order
+#pragma unroll
+    for (int m = 0; m < TM; ++m) {
+        const float n2 = nxp[m] + __shfl_xor(nxp[m], 32, kWave);
+        if (kg == 0) s_nx[wave][m * 32 + col] = n2;
+    }
+    __syncthreads();
     if (wave == 0) {
 #pragma unroll
         for (int m = 0; m < TM; ++m) {
-            const float n2 = nxp[m] + __shfl_xor(nxp[m], 32, kWave);
-            const int t = tok0 + m * 32 + col;
+            const int r = m * 32 + col;
+            const float n2 = ((s_nx[0][r] + s_nx[1][r]) + s_nx[2][r]) + s_nx[3][r];
+            const int t = tok0 + r;
             if (kg == 0 && t < T) nx[static_cast<int64_t>(sl) * T + t] = n2;
         }
     }
