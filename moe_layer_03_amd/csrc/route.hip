@@ -384,9 +384,9 @@ void launch_route_dt(const moe_shape& s, const XT* x, const XT* w, const float* 
             if (s.E <= 64) launch_fast<XT, 3, 1, 1, 8, 32, 3>(s, x, w, bias, idx, tw, logits, st);
             else launch_fast<XT, 3, 2, 1, 8, 32, 3>(s, x, w, bias, idx, tw, logits, st);
         } else {
-            // one chain per lane, deep prefetch: latency-bound small batches
-            if (s.E <= 64) launch_fast<XT, 1, 1, 1, 8, 32, 8>(s, x, w, bias, idx, tw, logits, st);
-            else launch_fast<XT, 1, 1, 2, 8, 32, 8>(s, x, w, bias, idx, tw, logits, st);
+            // one chain per lane, 64-row chunks (fewer per-chunk barriers), four-chunk prefetch
+            if (s.E <= 64) launch_fast<XT, 1, 1, 1, 8, 64, 4>(s, x, w, bias, idx, tw, logits, st);
+            else launch_fast<XT, 1, 1, 2, 8, 64, 4>(s, x, w, bias, idx, tw, logits, st);
         }
         return;
     }
