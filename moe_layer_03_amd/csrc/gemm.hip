@@ -353,16 +353,18 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 // workgroup owns one (expert, 64-column block) unit; its four waves split the
 // reduction into quarters and stream their weight fragments straight from the
 // fragment-packed weights into a register ring BD k-steps deep, together with
-// the matching fragments of up to 64 rows (two 32-row MFMA tiles; an expert
-// with more rows is handled in further 64-row groups).  The four partial
+// the matching fragments of up to 64 rows (one or two 32-row MFMA tiles; an
+// expert with more rows is handled in further row groups).  The four partial
 // tiles are added in wave order through LDS by all threads, which then apply
 // the epilogue.
 // ---------------------------------------------------------------------------
+template <int N> struct IntC { static constexpr int value = N; };
+
 template <int MODE, bool F16, int OUT, int BD>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p) {
     typedef typename OutType<OUT>::type OutT;
-    constexpr int MT = 2;                              // 32-row tiles per row group
-    __shared__ __attribute__((aligned(16))) float s_red[4][MT][2][16][64];
+    constexpr int MTMAX = 2;                           // 32-row tiles per row group, at most
+    __shared__ __attribute__((aligned(16))) float s_red[4][MTMAX][2][16][64];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -383,7 +385,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
         b_src[s2] = p.b + ((static_cast<int64_t>(e) * (p.N >> 5) + nb * 2 + s2) * kblocks + k0) * kFragElems +
                     lane * 8;
 
-    for (int g0 = 0; g0 < rows; g0 += 32 * MT) {
+    // one row group: MT 32-row tiles starting at row g0 of the segment (MT = 1
+    // when at most 32 rows remain, which is the usual case in decode)
+    auto group = [&](auto mt_tag, int g0) {
+        constexpr int MT = decltype(mt_tag)::value;
         const uint16_t* a_src[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -463,6 +468,15 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
             }
         }
         __syncthreads();                               // s_red reuse by the next row group
+    };
+    for (int g0 = 0; g0 < rows;) {
+        if (rows - g0 <= 32) {
+            group(IntC<1>{}, g0);
+            g0 += 32;
+        } else {
+            group(IntC<2>{}, g0);
+            g0 += 64;
+        }
     }
 }
 
