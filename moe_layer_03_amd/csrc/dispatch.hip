@@ -7,7 +7,8 @@
 // select the tokens routed to the rank's experts, aggregate the routing
 // information and prepare the tokens in the buffers the MoE GEMM reads.
 //
-// Four kernels, no host synchronisation:
+// Four kernels, no host synchronisation (batches of at most 16 chunks run
+// count, scan and scatter as one single-workgroup kernel):
 //   count   one wave per chunk of 64 tokens; for every local expert a wave
 //           ballot gives the bit mask of chunk tokens routed to it (a token
 //           picks an expert at most once) and its population count;
@@ -189,6 +190,85 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     }
 }
 
+// Small batches (at most 16 chunks, C * E_loc <= 4096): count, scan and
+// scatter in one workgroup with the chunk masks in LDS -- the same ballots,
+// prefix sums and stable ranks as the three kernels above, one launch.
+constexpr int kSmallChunks = kScanThreads / kWave;   // 16
+constexpr int kSmallCells = 4096;                    // C * E_loc
+
+__global__ __launch_bounds__(kScanThreads) void dispatch_small_kernel(const int32_t* __restrict__ topk_idx, int T,
+                                                                      int K, int e_begin, int E_loc, int C,
+                                                                      int32_t* __restrict__ counts,
+                                                                      int32_t* __restrict__ offsets,
+                                                                      int32_t* __restrict__ row_token,
+                                                                      int32_t* __restrict__ row_slot,
+                                                                      int32_t* __restrict__ slot_row) {
+    __shared__ uint64_t s_mask[kSmallCells];
+    __shared__ int s_base[kSmallCells];
+    __shared__ int s_tmp[17];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int c = tid >> 6;                            // chunk of this wave
+    const int t = c * kChunk + lane;
+    const bool valid = c < C && t < T;
+    // count: for every local expert, the mask of this chunk's tokens routed to it
+    if (c < C) {
+        const int words = (E_loc + kWave - 1) / kWave;
+        for (int wd = 0; wd < words; ++wd) {
+            uint64_t bits = 0;
+            if (valid) {
+                for (int j = 0; j < K; ++j) {
+                    const int i = topk_idx[static_cast<int64_t>(t) * K + j] - e_begin;
+                    if (i >= 0 && i < E_loc && (i >> 6) == wd) bits |= 1ull << (i & 63);
+                }
+            }
+            uint64_t mine = 0;
+            const int nb = min(kWave, E_loc - wd * kWave);
+            for (int b = 0; b < nb; ++b) {
+                const uint64_t m = __ballot((bits >> b) & 1ull);
+                if (lane == b) mine = m;
+            }
+            if (lane < nb) s_mask[c * E_loc + wd * kWave + lane] = mine;
+        }
+    }
+    __syncthreads();
+    // scan: per expert over chunks, then over experts
+    int total_i = 0;
+    for (int i = tid; i < E_loc; i += kScanThreads) {
+        int run = 0;
+        for (int cc = 0; cc < C; ++cc) {
+            s_base[cc * E_loc + i] = run;
+            run += __popcll(s_mask[cc * E_loc + i]);
+        }
+        counts[i] = run;
+        if (i == tid) total_i = run;
+    }
+    int all = 0;
+    const int pre = block_exclusive_scan_1024(tid < E_loc ? total_i : 0, s_tmp, &all);
+    if (tid < E_loc) {
+        offsets[tid] = pre;
+        for (int cc = 0; cc < C; ++cc) s_base[cc * E_loc + tid] += pre;
+    }
+    if (tid == 0) offsets[E_loc] = all;
+    __syncthreads();
+    // scatter: stable rank within the chunk from the mask
+    if (valid) {
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        for (int j = 0; j < K; ++j) {
+            const int64_t o = static_cast<int64_t>(t) * K + j;
+            const int i = topk_idx[o] - e_begin;
+            int row = -1;
+            if (i >= 0 && i < E_loc) {
+                const int cell = c * E_loc + i;
+                row = s_base[cell] + __popcll(s_mask[cell] & below);
+                row_token[row] = t;
+                row_slot[row] = j;
+            }
+            slot_row[o] = row;
+        }
+    }
+}
+
 template <typename XT>
 __global__ __launch_bounds__(256) void pack_kernel(const XT* __restrict__ x, int H,
                                                    const int32_t* __restrict__ row_token,
@@ -230,15 +310,20 @@ int launch_dispatch(const moe_shape& s, const int32_t* topk_idx, const void* x, 
     const int C = (s.T + kChunk - 1) / kChunk;
     Scratch sc = carve(s, scratch);
     const int g4 = (C + 3) / 4;
-    if (C > 0)
-        hipLaunchKernelGGL(count_kernel, dim3(g4), dim3(256), 0, st, topk_idx, s.T, s.K, s.e_begin, E_loc,
-                           sc.chunk_count, sc.chunk_mask, C);
-    // with no tokens the scan still runs and writes zero counts and offsets
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, sc.chunk_count, sc.chunk_base, C, E_loc,
-                       counts, offsets);
-    if (C > 0)
-        hipLaunchKernelGGL(scatter_kernel, dim3(g4), dim3(256), 0, st, topk_idx, s.T, s.K, s.e_begin, E_loc,
-                           sc.chunk_mask, sc.chunk_base, C, row_token, row_slot, slot_row);
+    if (C > 0 && C <= kSmallChunks && static_cast<int64_t>(C) * E_loc <= kSmallCells) {
+        hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kScanThreads), 0, st, topk_idx, s.T, s.K, s.e_begin,
+                           E_loc, C, counts, offsets, row_token, row_slot, slot_row);
+    } else {
+        if (C > 0)
+            hipLaunchKernelGGL(count_kernel, dim3(g4), dim3(256), 0, st, topk_idx, s.T, s.K, s.e_begin, E_loc,
+                               sc.chunk_count, sc.chunk_mask, C);
+        // with no tokens the scan still runs and writes zero counts and offsets
+        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, sc.chunk_count, sc.chunk_base, C, E_loc,
+                           counts, offsets);
+        if (C > 0)
+            hipLaunchKernelGGL(scatter_kernel, dim3(g4), dim3(256), 0, st, topk_idx, s.T, s.K, s.e_begin, E_loc,
+                               sc.chunk_mask, sc.chunk_base, C, row_token, row_slot, slot_row);
+    }
     if (x_packed != nullptr && C > 0) {
         const int64_t cap = static_cast<int64_t>(s.T) * min(s.K, E_loc);
         const int grid = static_cast<int>(cap < 4096 ? cap : 4096);

@@ -167,7 +167,11 @@ def test_route_from_logits_ties(B, E, K):
 
 @pytest.mark.parametrize("T,E,K,e0,e1,xdt", [(1000, 128, 8, 0, 32, "bf16"), (1000, 128, 8, 100, 128, "f32"),
                                              (130, 128, 8, 5, 6, "bf16"), (64, 8, 2, 0, 8, "f32"),
-                                             (3001, 1024, 16, 0, 1024, "bf16"), (77, 16, 16, 0, 16, "bf16")])
+                                             (3001, 1024, 16, 0, 1024, "bf16"), (77, 16, 16, 0, 16, "bf16"),
+                                             # one-workgroup dispatch (at most 16 chunks of 64 tokens and
+                                             # 4096 chunk-expert cells) at its limits, and just past them
+                                             (1024, 256, 8, 0, 256, "bf16"), (200, 512, 8, 0, 512, "bf16"),
+                                             (1025, 128, 8, 0, 128, "bf16"), (320, 1024, 8, 0, 1024, "bf16")])
 def test_dispatch_bit_exact(B, T, E, K, e0, e1, xdt):
     H = 128
     rng = np.random.default_rng(6)
