@@ -62,6 +62,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Same with a wave-uniform run-time bound n, LO <= n < HI (a binary search
 // over the immediate encodings: log2(HI - LO) scalar branches).
+// Wait until this wave's LDS and scalar-memory operations are done (vmcnt untouched).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 template <int LO, int HI>
 __device__ __forceinline__ void wait_vmcnt_bin(int n) {
     if constexpr (HI - LO == 1) {

@@ -24,6 +24,7 @@ namespace {
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kLdsFloatsW = 8192;   // 32 KiB of float32 router-weight staging
+constexpr int kChainMaxT = 1024;     // batches up to this size use one workgroup per token
 
 template <typename T> struct Widen;
 template <> struct Widen<uint16_t> {
@@ -341,6 +342,148 @@ __global__ __launch_bounds__(WAVES * 64) void route_fast_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches, E <= 128: one chain per lane, one workgroup per TPW tokens,
+// so that a batch of a hundred tokens still spreads over a hundred CUs and the
+// run time approaches the length of one dependent fma chain.  Each token is
+// served by WE = ceil(E / 64) waves (lane = expert).  The token rows are
+// widened to float32 in LDS once; the router weight streams through an NB-deep
+// ring of HC-row chunks (one contiguous run of HC * E elements each) copied
+// straight into LDS with 16-byte DMA, and every lane reads its expert's element
+// of each row.  Chunk indices past the end are clamped (harmless reloads into
+// stages already consumed), so every wave issues the same copies and the
+// vmcnt waits stay exact.
+// ---------------------------------------------------------------------------
+template <typename XT, int TPW, int WE, int HC, int NB, int XMAX>
+__global__ __launch_bounds__(TPW * WE * 64) void route_chain_kernel(
+    const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
+    int T, int H, int E, int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits) {
+    constexpr int NT = TPW * WE * 64;                        // threads
+    constexpr int VEC = 16 / sizeof(XT);                      // elements per 16-byte piece
+    constexpr int EP = WE * 64;                               // staged row stride (E padded)
+    constexpr int RP = EP / VEC;                              // pieces per staged row
+    constexpr int NPC = HC * RP / NT;                         // pieces per thread and chunk
+    constexpr int NXP = TPW * XMAX / VEC / NT;                // token-row pieces per thread
+    static_assert(HC * RP % NT == 0 && NPC >= 1, "chunk staging");
+    static_assert(NXP >= 1 && TPW * XMAX % (VEC * NT) == 0, "token staging");
+    static_assert(NB >= 2 && (NB - 2) * NPC < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) XT s_w[NB][HC * EP];
+    __shared__ __attribute__((aligned(16))) float s_x[TPW][XMAX];
+    __shared__ float s_l[WE > 1 ? TPW : 1][WE > 1 ? 128 : 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ti = wave / WE;                  // token slot of this wave
+    const int g = wave % WE;                   // expert group of this wave
+    const int e = g * kWave + lane;
+    const int ec = min(e, E - 1);              // lanes past E compute a copy of the last column, unused
+    const int tok0 = blockIdx.x * TPW;
+    const int nc = H / HC;
+    const int rp = E / VEC;                    // pieces per row of this E
+
+    // staged slot p = (row, piece) of the padded layout; pieces past the row's
+    // end copy the row's last piece into the padding, which nobody reads
+    int src_off[NPC];
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+        const int p = i * NT + tid;
+        src_off[i] = (p / RP) * E + min(p % RP, rp - 1) * VEC;
+    }
+    auto issue = [&](int c, int stage) {
+        const XT* src = w + static_cast<int64_t>(c) * HC * E;
+#pragma unroll
+        for (int i = 0; i < NPC; ++i)
+            dma16(reinterpret_cast<const uint16_t*>(src + src_off[i]),
+                  reinterpret_cast<uint16_t*>(&s_w[stage][(i * NT + wave * kWave) * VEC]));
+    };
+
+    // token rows: loads first (rows and columns clamped to valid memory), then
+    // the first chunks; row r's columns past H land in unused staging
+    constexpr int XP = XMAX / VEC;             // pieces in one staged row
+    u32x4 xr[NXP];
+#pragma unroll
+    for (int j = 0; j < NXP; ++j) {
+        const int i = j * NT + tid;
+        const int t = min(tok0 + i / XP, T - 1);
+        const int col = min((i % XP) * VEC, H - VEC);
+        xr[j] = *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t) * H + col);
+    }
+#pragma unroll
+    for (int q = 0; q < NB - 1; ++q) issue(min(q, nc - 1), q);
+#pragma unroll
+    for (int j = 0; j < NXP; ++j) {
+        const int i = j * NT + tid;
+        const bool live = tok0 + i / XP < T;
+        float* dst = &s_x[i / XP][(i % XP) * VEC];
+        if constexpr (sizeof(XT) == 2) {
+            floatx4 a, b;
+            a[0] = __uint_as_float(xr[j][0] << 16); a[1] = __uint_as_float(xr[j][0] & 0xFFFF0000u);
+            a[2] = __uint_as_float(xr[j][1] << 16); a[3] = __uint_as_float(xr[j][1] & 0xFFFF0000u);
+            b[0] = __uint_as_float(xr[j][2] << 16); b[1] = __uint_as_float(xr[j][2] & 0xFFFF0000u);
+            b[2] = __uint_as_float(xr[j][3] << 16); b[3] = __uint_as_float(xr[j][3] & 0xFFFF0000u);
+            if (!live) a = b = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            *reinterpret_cast<floatx4*>(dst) = a;
+            *reinterpret_cast<floatx4*>(dst + 4) = b;
+        } else {
+            floatx4 a = __builtin_bit_cast(floatx4, xr[j]);
+            if (!live) a = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            *reinterpret_cast<floatx4*>(dst) = a;
+        }
+    }
+    wait_lgkmcnt0();   // the staged rows are written before the first barrier
+
+    float acc = 0.0f;
+    const float* sx = s_x[ti];
+    for (int c = 0; c < nc; ++c) {
+        wait_vmcnt<(NB - 2) * NPC>();          // this wave's copies of chunk c have landed
+        __builtin_amdgcn_s_barrier();          // ... everyone's (and the token rows); stage c-1 is free
+        issue(min(c + NB - 1, nc - 1), (c + NB - 1) % NB);
+        const XT* sw = s_w[c % NB] + ec;
+        const float* xc = sx + c * HC;
+        // groups of 8 rows: the reads of group q+1 are in flight while group q's
+        // fmas run (at most 15 LDS reads may be outstanding per wave)
+        XT wv[2][8];
+        floatx4 xv[2][2];
+        auto fetch = [&](int q, int slot) {
+            xv[slot][0] = *reinterpret_cast<const floatx4*>(xc + q * 8);
+            xv[slot][1] = *reinterpret_cast<const floatx4*>(xc + q * 8 + 4);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wv[slot][j] = sw[(q * 8 + j) * EP];
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int q = 0; q < HC / 8; ++q) {
+            if (q + 1 < HC / 8) fetch(q + 1, (q + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc = fmaf(xv[q & 1][j >> 2][j & 3], Widen<XT>::f(wv[q & 1][j]), acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is released
+
+    const int t = tok0 + ti;
+    float v = acc;
+    if (bias != nullptr && e < E) v = v + bias[e];
+    if (logits != nullptr && e < E && t < T) logits[static_cast<int64_t>(t) * E + e] = v;
+    if constexpr (WE == 1) {
+        if (t < T) {
+            float l[1] = {v};
+            select_and_write<1>(l, E, K, t, topk_idx, topk_w);
+        }
+    } else {
+        static_assert(WE == 2, "E <= 128");
+        s_l[ti][e] = v;
+        __syncthreads();
+        if (g == 0 && t < T) {
+            float l[2] = {s_l[ti][lane], s_l[ti][kWave + lane]};
+            select_and_write<2>(l, E, K, t, topk_idx, topk_w);
+        }
+    }
+}
+
 template <int NE>
 __global__ __launch_bounds__(kRouteThreads) void select_kernel(
     const float* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ topk_idx,
@@ -375,9 +518,24 @@ void launch_fast(const moe_shape& s, const XT* x, const XT* w, const float* bias
                        w, bias, s.T, s.H, s.E, s.K, idx, tw, logits);
 }
 
+template <typename XT, int TPW, int WE, int HC, int NB, int XMAX>
+void launch_chain(const moe_shape& s, const XT* x, const XT* w, const float* bias, int32_t* idx, float* tw,
+                  float* logits, hipStream_t st) {
+    const int grid = (s.T + TPW - 1) / TPW;
+    hipLaunchKernelGGL((route_chain_kernel<XT, TPW, WE, HC, NB, XMAX>), dim3(grid), dim3(TPW * WE * 64), 0, st, x,
+                       w, bias, s.T, s.H, s.E, s.K, idx, tw, logits);
+}
+
 template <typename XT>
 void launch_route_dt(const moe_shape& s, const XT* x, const XT* w, const float* bias, int32_t* idx,
                      float* tw, float* logits, hipStream_t st) {
+    // rows of the router weight must split into 16-byte pieces (E a multiple of 8 for bf16, 4 for float32)
+    if (s.E <= 128 && s.E % (16 / sizeof(XT)) == 0 && s.T <= kChainMaxT && s.H <= 4096) {
+        // one token per workgroup: chains spread over as many CUs as there are tokens
+        if (s.E <= 64) launch_chain<XT, 1, 1, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, st);
+        else launch_chain<XT, 1, 2, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, st);
+        return;
+    }
     if (s.E <= 128) {
         if (s.T >= 2048) {
             // 8 waves x 3 tokens per workgroup: about two waves per SIMD at 6000 tokens

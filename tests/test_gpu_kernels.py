@@ -47,6 +47,18 @@ def test_route_bit_exact_bf16(B, T, H, E, K):
     assert np.abs(tw - rw).max() <= 1e-6
 
 
+@pytest.mark.parametrize("T,H,E,K,dt", [(1, 4096, 128, 8, "bf16"), (128, 4096, 128, 8, "bf16"),
+                                        (1024, 256, 128, 8, "bf16"), (7, 128, 72, 4, "bf16"),
+                                        (33, 64, 24, 2, "f32"), (100, 320, 64, 64, "f32"), (50, 4096, 16, 16, "f32"),
+                                        (65, 192, 120, 8, "f32")])
+def test_route_small_batch_bit_exact(B, T, H, E, K, dt):
+    """Batches of at most 1024 tokens: one workgroup per token, rows staged with padding past E."""
+    idx, tw, lg, ri, rw, rl = _route_case(B, T, H, E, K, dtype=dt, seed=T + E)
+    assert np.array_equal(lg.view(np.uint32), rl.view(np.uint32)), "logits differ from the fixed fma order"
+    assert np.array_equal(idx, ri)
+    assert np.abs(tw - rw).max() <= 1e-6
+
+
 def test_route_bit_exact_f32_tiny(B):
     wl = W.WORKLOADS["tiny"]
     x, w = W.gen_x(wl), W.gen_router(wl)
