@@ -18,6 +18,9 @@
 // 64-bit max reductions over (orderable logit, ~expert) keys.
 #include "common.hpp"
 
+#include <type_traits>
+#include <utility>
+
 namespace moe {
 namespace {
 
@@ -345,29 +348,122 @@ __global__ __launch_bounds__(WAVES * 64) void route_fast_kernel(
 // ---------------------------------------------------------------------------
 // Small batches, E <= 128: one chain per lane, one workgroup per TPW tokens,
 // so that a batch of a hundred tokens still spreads over a hundred CUs and the
-// run time approaches the length of one dependent fma chain.  Each token is
-// served by WE = ceil(E / 64) waves (lane = expert).  The token rows are
-// widened to float32 in LDS once; the router weight streams through an NB-deep
-// ring of HC-row chunks (one contiguous run of HC * E elements each) copied
-// straight into LDS with 16-byte DMA, and every lane reads its expert's element
-// of each row.  Chunk indices past the end are clamped (harmless reloads into
-// stages already consumed), so every wave issues the same copies and the
-// vmcnt waits stay exact.
+// run time approaches the length of one dependent fma chain.
+//
+// A workgroup has CW = TPW * WE chain waves (token ti, experts g*64 + lane)
+// and DW copy waves.  The copy waves stream the router weight through an
+// NB-deep ring of HC-row chunks straight into LDS (16-byte DMA; rows padded to
+// EP = 64 * WE elements), so the chain waves spend their issue slots on little
+// besides v_fmac and LDS reads.  The token rows are widened to float32 in LDS
+// once.  Per group of 8 rows a chain wave waits for that group's operands and
+// then alternates its 8 dependent fmas with the 10 reads of the group two
+// ahead (4 register slots): between two dependent fmas the wave has an issue
+// slot to spare, which the reads fill.  A bf16 weight is read into the high
+// half of a register whose low half is zero from the start, which is exactly
+// its float32 value.
 // ---------------------------------------------------------------------------
-template <typename XT, int TPW, int WE, int HC, int NB, int XMAX>
-__global__ __launch_bounds__(TPW * WE * 64) void route_chain_kernel(
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The group's own operands (x0, x1, w) are used after at most N younger LDS
+// reads remain outstanding (reads return in order); the next operands (nx0,
+// nx1, nw) are written when their reads land, two groups later.
+#define MOE_CHAIN_GROUP(RD)                                                                                     \
+    asm volatile("s_waitcnt lgkmcnt(%[n])\n\t"                                                                \
+                 "v_fmac_f32 %[acc], %[a0], %[w0]\n\t"                                                        \
+                 "ds_read_b128 %[nx0], %[ax] offset:%[ox0]\n\t"                                               \
+                 "v_fmac_f32 %[acc], %[a1], %[w1]\n\t"                                                        \
+                 "ds_read_b128 %[nx1], %[ax] offset:%[ox1]\n\t"                                               \
+                 "v_fmac_f32 %[acc], %[a2], %[w2]\n\t"                                                        \
+                 RD " %[n0], %[aw] offset:%[o0]\n\t"                                                          \
+                 "v_fmac_f32 %[acc], %[a3], %[w3]\n\t"                                                        \
+                 RD " %[n1], %[aw] offset:%[o1]"                                                              \
+                 : [acc] "+v"(acc), [nx0] "=&v"(nx0), [nx1] "=&v"(nx1), [n0] "+v"(nw[0]), [n1] "+v"(nw[1])    \
+                 : [a0] "v"(x0[0]), [a1] "v"(x0[1]), [a2] "v"(x0[2]), [a3] "v"(x0[3]), [w0] "v"(w[0]),       \
+                   [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [ax] "v"(ax), [aw] "v"(aw), [n] "i"(N),   \
+                   [ox0] "i"(OX), [ox1] "i"(OX + 16), [o0] "i"(OW), [o1] "i"(OW + RB));                        \
+    asm volatile("v_fmac_f32 %[acc], %[a4], %[w4]\n\t"                                                        \
+                 RD " %[n2], %[aw] offset:%[o2]\n\t"                                                          \
+                 "v_fmac_f32 %[acc], %[a5], %[w5]\n\t"                                                        \
+                 RD " %[n3], %[aw] offset:%[o3]\n\t"                                                          \
+                 "v_fmac_f32 %[acc], %[a6], %[w6]\n\t"                                                        \
+                 RD " %[n4], %[aw] offset:%[o4]\n\t"                                                          \
+                 "v_fmac_f32 %[acc], %[a7], %[w7]\n\t"                                                        \
+                 RD " %[n5], %[aw] offset:%[o5]\n\t"                                                          \
+                 RD " %[n6], %[aw] offset:%[o6]\n\t"                                                          \
+                 RD " %[n7], %[aw] offset:%[o7]"                                                              \
+                 : [acc] "+v"(acc), [n2] "+v"(nw[2]), [n3] "+v"(nw[3]), [n4] "+v"(nw[4]), [n5] "+v"(nw[5]),  \
+                   [n6] "+v"(nw[6]), [n7] "+v"(nw[7])                                                         \
+                 : [a4] "v"(x1[0]), [a5] "v"(x1[1]), [a6] "v"(x1[2]), [a7] "v"(x1[3]), [w4] "v"(w[4]),       \
+                   [w5] "v"(w[5]), [w6] "v"(w[6]), [w7] "v"(w[7]), [aw] "v"(aw), [o2] "i"(OW + 2 * RB),      \
+                   [o3] "i"(OW + 3 * RB), [o4] "i"(OW + 4 * RB), [o5] "i"(OW + 5 * RB), [o6] "i"(OW + 6 * RB), \
+                   [o7] "i"(OW + 7 * RB))
+
+template <bool BF16, int N, int RB, int OX, int OW>
+__device__ __forceinline__ void chain_group(float& acc, const floatx4& x0, const floatx4& x1, const float (&w)[8],
+                                            floatx4& nx0, floatx4& nx1, float (&nw)[8], uint32_t ax, uint32_t aw) {
+    if constexpr (BF16) {
+        MOE_CHAIN_GROUP("ds_read_u16_d16_hi");
+    } else {
+        MOE_CHAIN_GROUP("ds_read_b32");
+    }
+}
+#undef MOE_CHAIN_GROUP
+
+// The reads of one group with no fmas (the first two groups of the chain).
+#define MOE_CHAIN_FETCH(RD)                                                                                     \
+    asm volatile("ds_read_b128 %[nx0], %[ax] offset:%[ox0]\n\t"                                               \
+                 "ds_read_b128 %[nx1], %[ax] offset:%[ox1]\n\t"                                               \
+                 RD " %[n0], %[aw] offset:%[o0]\n\t"                                                          \
+                 RD " %[n1], %[aw] offset:%[o1]\n\t"                                                          \
+                 RD " %[n2], %[aw] offset:%[o2]\n\t"                                                          \
+                 RD " %[n3], %[aw] offset:%[o3]\n\t"                                                          \
+                 RD " %[n4], %[aw] offset:%[o4]\n\t"                                                          \
+                 RD " %[n5], %[aw] offset:%[o5]\n\t"                                                          \
+                 RD " %[n6], %[aw] offset:%[o6]\n\t"                                                          \
+                 RD " %[n7], %[aw] offset:%[o7]"                                                              \
+                 : [nx0] "=&v"(nx0), [nx1] "=&v"(nx1), [n0] "+v"(nw[0]), [n1] "+v"(nw[1]), [n2] "+v"(nw[2]),  \
+                   [n3] "+v"(nw[3]), [n4] "+v"(nw[4]), [n5] "+v"(nw[5]), [n6] "+v"(nw[6]), [n7] "+v"(nw[7])   \
+                 : [ax] "v"(ax), [aw] "v"(aw), [ox0] "i"(OX), [ox1] "i"(OX + 16), [o0] "i"(OW),               \
+                   [o1] "i"(OW + RB), [o2] "i"(OW + 2 * RB), [o3] "i"(OW + 3 * RB), [o4] "i"(OW + 4 * RB),    \
+                   [o5] "i"(OW + 5 * RB), [o6] "i"(OW + 6 * RB), [o7] "i"(OW + 7 * RB))
+
+template <bool BF16, int RB, int OX, int OW>
+__device__ __forceinline__ void chain_fetch(floatx4& nx0, floatx4& nx1, float (&nw)[8], uint32_t ax, uint32_t aw) {
+    if constexpr (BF16) {
+        MOE_CHAIN_FETCH("ds_read_u16_d16_hi");
+    } else {
+        MOE_CHAIN_FETCH("ds_read_b32");
+    }
+}
+#undef MOE_CHAIN_FETCH
+
+template <typename XT, int TPW, int WE, int DW, int HC, int NB, int XMAX>
+__global__ __launch_bounds__((TPW * WE + DW) * 64) void route_chain_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
     int T, int H, int E, int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ logits) {
-    constexpr int NT = TPW * WE * 64;                        // threads
+    constexpr bool BF16 = sizeof(XT) == 2;
+    constexpr int CW = TPW * WE;                              // chain waves
+    constexpr int CT = CW * 64;                               // chain threads
+    constexpr int DT = DW * 64;                               // copy threads
     constexpr int VEC = 16 / sizeof(XT);                      // elements per 16-byte piece
     constexpr int EP = WE * 64;                               // staged row stride (E padded)
+    constexpr int RB = EP * static_cast<int>(sizeof(XT));     // bytes per staged row
     constexpr int RP = EP / VEC;                              // pieces per staged row
-    constexpr int NPC = HC * RP / NT;                         // pieces per thread and chunk
-    constexpr int NXP = TPW * XMAX / VEC / NT;                // token-row pieces per thread
-    static_assert(HC * RP % NT == 0 && NPC >= 1, "chunk staging");
-    static_assert(NXP >= 1 && TPW * XMAX % (VEC * NT) == 0, "token staging");
-    static_assert(NB >= 2 && (NB - 2) * NPC < 64, "vmcnt range");
+    constexpr int NPC = HC * RP / DT;                         // pieces per copy thread and chunk
+    constexpr int NXP = TPW * XMAX / VEC / CT;                // token-row pieces per chain thread
+    constexpr int GPC = HC / 8;                               // row groups per chunk
+    static_assert(HC * RP % DT == 0 && NPC >= 1, "chunk staging");
+    static_assert(NXP >= 1 && TPW * XMAX % (VEC * CT) == 0, "token staging");
+    static_assert(NB >= 3 && (NB - 2) * NPC < 64, "one chunk of look-ahead; vmcnt range");
+    static_assert(GPC % 4 == 0 && HC * RB < 65536, "register slots; LDS offsets");
     __shared__ __attribute__((aligned(16))) XT s_w[NB][HC * EP];
     __shared__ __attribute__((aligned(16))) float s_x[TPW][XMAX];
     __shared__ float s_l[WE > 1 ? TPW : 1][WE > 1 ? 128 : 1];
@@ -375,111 +471,133 @@ __global__ __launch_bounds__(TPW * WE * 64) void route_chain_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ti = wave / WE;                  // token slot of this wave
-    const int g = wave % WE;                   // expert group of this wave
-    const int e = g * kWave + lane;
-    const int ec = min(e, E - 1);              // lanes past E compute a copy of the last column, unused
     const int tok0 = blockIdx.x * TPW;
     const int nc = H / HC;
-    const int rp = E / VEC;                    // pieces per row of this E
-
-    // staged slot p = (row, piece) of the padded layout; pieces past the row's
-    // end copy the row's last piece into the padding, which nobody reads
-    int src_off[NPC];
-#pragma unroll
-    for (int i = 0; i < NPC; ++i) {
-        const int p = i * NT + tid;
-        src_off[i] = (p / RP) * E + min(p % RP, rp - 1) * VEC;
-    }
-    auto issue = [&](int c, int stage) {
-        const XT* src = w + static_cast<int64_t>(c) * HC * E;
-#pragma unroll
-        for (int i = 0; i < NPC; ++i)
-            dma16(reinterpret_cast<const uint16_t*>(src + src_off[i]),
-                  reinterpret_cast<uint16_t*>(&s_w[stage][(i * NT + wave * kWave) * VEC]));
-    };
-
-    // token rows: loads first (rows and columns clamped to valid memory), then
-    // the first chunks; row r's columns past H land in unused staging
-    constexpr int XP = XMAX / VEC;             // pieces in one staged row
-    u32x4 xr[NXP];
-#pragma unroll
-    for (int j = 0; j < NXP; ++j) {
-        const int i = j * NT + tid;
-        const int t = min(tok0 + i / XP, T - 1);
-        const int col = min((i % XP) * VEC, H - VEC);
-        xr[j] = *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t) * H + col);
-    }
-#pragma unroll
-    for (int q = 0; q < NB - 1; ++q) issue(min(q, nc - 1), q);
-#pragma unroll
-    for (int j = 0; j < NXP; ++j) {
-        const int i = j * NT + tid;
-        const bool live = tok0 + i / XP < T;
-        float* dst = &s_x[i / XP][(i % XP) * VEC];
-        if constexpr (sizeof(XT) == 2) {
-            floatx4 a, b;
-            a[0] = __uint_as_float(xr[j][0] << 16); a[1] = __uint_as_float(xr[j][0] & 0xFFFF0000u);
-            a[2] = __uint_as_float(xr[j][1] << 16); a[3] = __uint_as_float(xr[j][1] & 0xFFFF0000u);
-            b[0] = __uint_as_float(xr[j][2] << 16); b[1] = __uint_as_float(xr[j][2] & 0xFFFF0000u);
-            b[2] = __uint_as_float(xr[j][3] << 16); b[3] = __uint_as_float(xr[j][3] & 0xFFFF0000u);
-            if (!live) a = b = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-            *reinterpret_cast<floatx4*>(dst) = a;
-            *reinterpret_cast<floatx4*>(dst + 4) = b;
-        } else {
-            floatx4 a = __builtin_bit_cast(floatx4, xr[j]);
-            if (!live) a = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-            *reinterpret_cast<floatx4*>(dst) = a;
-        }
-    }
-    wait_lgkmcnt0();   // the staged rows are written before the first barrier
-
     float acc = 0.0f;
-    const float* sx = s_x[ti];
-    for (int c = 0; c < nc; ++c) {
-        wait_vmcnt<(NB - 2) * NPC>();          // this wave's copies of chunk c have landed
-        __builtin_amdgcn_s_barrier();          // ... everyone's (and the token rows); stage c-1 is free
-        issue(min(c + NB - 1, nc - 1), (c + NB - 1) % NB);
-        const XT* sw = s_w[c % NB] + ec;
-        const float* xc = sx + c * HC;
-        // groups of 8 rows: the reads of group q+1 are in flight while group q's
-        // fmas run (at most 15 LDS reads may be outstanding per wave)
-        XT wv[2][8];
-        floatx4 xv[2][2];
-        auto fetch = [&](int q, int slot) {
-            xv[slot][0] = *reinterpret_cast<const floatx4*>(xc + q * 8);
-            xv[slot][1] = *reinterpret_cast<const floatx4*>(xc + q * 8 + 4);
+
+    if (wave >= CW) {
+        // ---- copy waves: chunk c lands in stage c % NB; chunk indices past the
+        // end are clamped (harmless reloads into stages already consumed), so
+        // every copy wave issues the same copies and the vmcnt waits stay exact
+        const int dt = tid - CT;
+        const int rp = E / VEC;                // pieces per row of this E
+        int src_off[NPC];                      // pieces past a row's end copy its last piece into the padding
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wv[slot][j] = sw[(q * 8 + j) * EP];
+        for (int i = 0; i < NPC; ++i) {
+            const int p = i * DT + dt;
+            src_off[i] = (p / RP) * E + min(p % RP, rp - 1) * VEC;
+        }
+        auto issue = [&](int c, int stage) {
+            const XT* src = w + static_cast<int64_t>(c) * HC * E;
+#pragma unroll
+            for (int i = 0; i < NPC; ++i)
+                dma16(reinterpret_cast<const uint16_t*>(src + src_off[i]),
+                      reinterpret_cast<uint16_t*>(&s_w[stage][(i * DT + (wave - CW) * kWave) * VEC]));
         };
-        fetch(0, 0);
 #pragma unroll
-        for (int q = 0; q < HC / 8; ++q) {
-            if (q + 1 < HC / 8) fetch(q + 1, (q + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < NB - 1; ++q) issue(min(q, nc - 1), q);
+        wait_vmcnt<(NB - 2) * NPC>();          // chunk 0 has landed
+        __builtin_amdgcn_s_barrier();
+        for (int c = 0; c < nc; ++c) {
+            wait_vmcnt<(NB - 3) * NPC>();      // chunk c+1 has landed
+            __builtin_amdgcn_s_barrier();      // ... and every chain wave is done with stage c-1
+            issue(min(c + NB - 1, nc - 1), (c + NB - 1) % NB);
+        }
+        wait_vmcnt<0>();                       // no copy may land after the workgroup's LDS is released
+    } else {
+        // ---- chain waves
+        const int ti = wave / WE;
+        const int ec = min((wave % WE) * kWave + lane, E - 1);   // lanes past E repeat the last column, unused
+        // token rows -> float32 (rows past T are zero; columns past H land in unused staging)
+        constexpr int XP = XMAX / VEC;
+        u32x4 xr[NXP];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc = fmaf(xv[q & 1][j >> 2][j & 3], Widen<XT>::f(wv[q & 1][j]), acc);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < NXP; ++j) {
+            const int i = j * CT + tid;
+            const int t = min(tok0 + i / XP, T - 1);
+            const int col = min((i % XP) * VEC, H - VEC);
+            xr[j] = *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t) * H + col);
+        }
+#pragma unroll
+        for (int j = 0; j < NXP; ++j) {
+            const int i = j * CT + tid;
+            const bool live = tok0 + i / XP < T;
+            float* dst = &s_x[i / XP][(i % XP) * VEC];
+            if constexpr (BF16) {
+                floatx4 a, b;
+                a[0] = __uint_as_float(xr[j][0] << 16); a[1] = __uint_as_float(xr[j][0] & 0xFFFF0000u);
+                a[2] = __uint_as_float(xr[j][1] << 16); a[3] = __uint_as_float(xr[j][1] & 0xFFFF0000u);
+                b[0] = __uint_as_float(xr[j][2] << 16); b[1] = __uint_as_float(xr[j][2] & 0xFFFF0000u);
+                b[2] = __uint_as_float(xr[j][3] << 16); b[3] = __uint_as_float(xr[j][3] & 0xFFFF0000u);
+                if (!live) a = b = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                *reinterpret_cast<floatx4*>(dst) = a;
+                *reinterpret_cast<floatx4*>(dst + 4) = b;
+            } else {
+                floatx4 a = __builtin_bit_cast(floatx4, xr[j]);
+                if (!live) a = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                *reinterpret_cast<floatx4*>(dst) = a;
+            }
+        }
+        wait_lgkmcnt0();                       // the staged rows are written before the barrier
+
+        floatx4 xv[4][2];
+        float wv[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wv[k][j] = 0.0f;   // low halves stay zero (bf16 reads fill the high half)
+        auto lds = [](const void* p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)); };
+        const uint32_t ax0 = lds(s_x[ti]);
+        const uint32_t aw0 = lds(&s_w[0][ec]);
+        constexpr uint32_t kStage = HC * EP * sizeof(XT);
+
+        __builtin_amdgcn_s_barrier();          // chunk 0 and the token rows are in LDS
+        chain_fetch<BF16, RB, 0, 0>(xv[0][0], xv[0][1], wv[0], ax0, aw0);
+        chain_fetch<BF16, RB, 32, 8 * RB>(xv[1][0], xv[1][1], wv[1], ax0, aw0);
+        for (int c = 0; c < nc; ++c) {
+            __builtin_amdgcn_s_barrier();      // chunk c+1 is in LDS; stage c-1 may be refilled
+            const uint32_t axc = ax0 + c * HC * 4;
+            const uint32_t axn = ax0 + min(c + 1, nc - 1) * HC * 4;
+            const uint32_t awc = aw0 + (c % NB) * kStage;
+            const uint32_t awn = aw0 + ((c + 1) % NB) * kStage;
+            static_for<GPC>([&](auto qc) {
+                constexpr int Q = decltype(qc)::value;
+                constexpr int S = Q % 4, NS = (Q + 2) % 4, QN = (Q + 2) % GPC;
+                constexpr bool NEXT = Q + 2 >= GPC;
+                chain_group<BF16, 10, RB, QN * 32, QN * 8 * RB>(acc, xv[S][0], xv[S][1], wv[S], xv[NS][0],
+                                                                xv[NS][1], wv[NS], NEXT ? axn : axc,
+                                                                NEXT ? awn : awc);
+            });
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the look-ahead reads past the end
+    }
+
+    if (wave < CW) {
+        const int ti = wave / WE;
+        const int e = (wave % WE) * kWave + lane;
+        const int t = tok0 + ti;
+        float v = acc;
+        if (bias != nullptr && e < E) v = v + bias[e];
+        if (logits != nullptr && e < E && t < T) logits[static_cast<int64_t>(t) * E + e] = v;
+        if constexpr (WE == 1) {
+            if (t < T) {
+                float l[1] = {v};
+                select_and_write<1>(l, E, K, t, topk_idx, topk_w);
+            }
+        } else {
+            s_l[ti][e] = v;
         }
     }
-    wait_vmcnt<0>();   // no copy may land after the workgroup's LDS is released
-
-    const int t = tok0 + ti;
-    float v = acc;
-    if (bias != nullptr && e < E) v = v + bias[e];
-    if (logits != nullptr && e < E && t < T) logits[static_cast<int64_t>(t) * E + e] = v;
-    if constexpr (WE == 1) {
-        if (t < T) {
-            float l[1] = {v};
-            select_and_write<1>(l, E, K, t, topk_idx, topk_w);
-        }
-    } else {
+    if constexpr (WE > 1) {
         static_assert(WE == 2, "E <= 128");
-        s_l[ti][e] = v;
         __syncthreads();
-        if (g == 0 && t < T) {
-            float l[2] = {s_l[ti][lane], s_l[ti][kWave + lane]};
-            select_and_write<2>(l, E, K, t, topk_idx, topk_w);
+        if (wave < CW && wave % WE == 0) {
+            const int ti = wave / WE;
+            const int t = tok0 + ti;
+            if (t < T) {
+                float l[2] = {s_l[ti][lane], s_l[ti][kWave + lane]};
+                select_and_write<2>(l, E, K, t, topk_idx, topk_w);
+            }
         }
     }
 }
@@ -518,12 +636,12 @@ void launch_fast(const moe_shape& s, const XT* x, const XT* w, const float* bias
                        w, bias, s.T, s.H, s.E, s.K, idx, tw, logits);
 }
 
-template <typename XT, int TPW, int WE, int HC, int NB, int XMAX>
+template <typename XT, int TPW, int WE, int DW, int HC, int NB, int XMAX>
 void launch_chain(const moe_shape& s, const XT* x, const XT* w, const float* bias, int32_t* idx, float* tw,
                   float* logits, hipStream_t st) {
     const int grid = (s.T + TPW - 1) / TPW;
-    hipLaunchKernelGGL((route_chain_kernel<XT, TPW, WE, HC, NB, XMAX>), dim3(grid), dim3(TPW * WE * 64), 0, st, x,
-                       w, bias, s.T, s.H, s.E, s.K, idx, tw, logits);
+    hipLaunchKernelGGL((route_chain_kernel<XT, TPW, WE, DW, HC, NB, XMAX>), dim3(grid), dim3((TPW * WE + DW) * 64),
+                       0, st, x, w, bias, s.T, s.H, s.E, s.K, idx, tw, logits);
 }
 
 template <typename XT>
@@ -532,8 +650,8 @@ void launch_route_dt(const moe_shape& s, const XT* x, const XT* w, const float* 
     // rows of the router weight must split into 16-byte pieces (E a multiple of 8 for bf16, 4 for float32)
     if (s.E <= 128 && s.E % (16 / sizeof(XT)) == 0 && s.T <= kChainMaxT && s.H <= 4096) {
         // one token per workgroup: chains spread over as many CUs as there are tokens
-        if (s.E <= 64) launch_chain<XT, 1, 1, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, st);
-        else launch_chain<XT, 1, 2, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, st);
+        if (s.E <= 64) launch_chain<XT, 1, 1, 1, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, st);
+        else launch_chain<XT, 1, 2, 2, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, st);
         return;
     }
     if (s.E <= 128) {
