@@ -27,9 +27,11 @@
 //     stages (~120 KiB per CU) are in flight: load throughput per CU is bound by
 //     bytes in flight, and this keeps it above what the MFMAs consume;
 //   * weights (B) are packed once in MFMA fragment order (one 1 KiB block per
-//     32 columns x 16 k, lane-major): every copy and every fragment read is one
-//     contiguous, conflict-free 1 KiB per wave, and each wave reads only its
-//     own columns;
+//     32 columns x 16 k, lane-major), the two 32-column halves of each
+//     64-column block side by side per 16 k: every copy and every fragment
+//     read is one contiguous, conflict-free 1 KiB per wave, each wave reads
+//     only its own columns, and a 64-column block's weights are one
+//     contiguous run;
 //   * fragments are read from LDS one k-step ahead of the MFMAs that use them,
 //     and the once-per-stage barrier sits between a stage's two k-steps, so it
 //     waits while MFMAs are still executing and every stage starts with its
@@ -62,13 +64,20 @@ constexpr int KG = BK / 8;             // 16-byte granules per row of a stage
 constexpr int kMaxExperts = 1024;
 constexpr int kFragElems = 512;        // one 32-column x 16-k fragment block (64 lanes x 8)
 
+// Packed weights: fragment block of expert e, 32-column tile n32 and 16-k block
+// kb, in [E_loc][N/64][Kd/16][2] order (the pair of 32-column tiles of a
+// 64-column block sits side by side at every kb).
+__device__ __forceinline__ int64_t frag_block(int e, int n32, int kb, int N, int kblocks) {
+    return ((static_cast<int64_t>(e) * (N >> 6) + (n32 >> 1)) * kblocks + kb) * 2 + (n32 & 1);
+}
+
 enum Mode { kPlain = 0, kGateUpPlain = 1, kSwiGLU = 2 };
 enum Out { kOutF32 = 0, kOutBF16 = 1, kOutF16 = 2 };
 
 struct GemmArgs {
     const uint16_t* a;         // [rows][Kd] 16-bit
     const int32_t* a_rows;     // NULL, or: packed row r reads row a_rows[r] of a (gather)
-    const uint16_t* b;         // [E_loc][N/32][Kd/16] fragment blocks
+    const uint16_t* b;         // [E_loc][N/64][Kd/16][2] fragment blocks
     const int32_t* offsets;    // [E_loc + 1]
     void* c;                   // output rows
     int E_loc;
@@ -238,8 +247,8 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
         const uint16_t* b_src[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-            b_src[s2] = p.b + ((static_cast<int64_t>(e) * (p.N >> 5) + ((n_tile * BN + bq * 64) >> 5) + s2) * kblocks) *
-                                  kFragElems + lane * 8;
+            b_src[s2] = p.b + frag_block(e, ((n_tile * BN + bq * 64) >> 5) + s2, 0, p.N, kblocks) * kFragElems +
+                        lane * 8;
         // issue the copies of k-tile kt into ring stage st
         auto issue = [&](int kt, int st) {
 #pragma unroll
@@ -247,7 +256,7 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int d = 0; d < B_DMA; ++d) {
                 const int j = jb + d;
-                dma16(b_src[j & 1] + static_cast<int64_t>(kt * KS + (j >> 1)) * kFragElems, &s_b[st][bq][j][0]);
+                dma16(b_src[j & 1] + static_cast<int64_t>(kt * KS + (j >> 1)) * 2 * kFragElems, &s_b[st][bq][j][0]);
             }
         };
         auto read_frags = [&](u32x4 (&fa)[TM], u32x4 (&fb)[2], int st, int ks) {
@@ -376,14 +385,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
     if (rows <= 0) return;                             // uniform over the workgroup
 
     const int nks = p.Kd >> 4;                         // k-steps (a multiple of 4)
-    const int kq = nks >> 2;                           // k-steps of this wave
-    const int k0 = wave * kq;
+    const int kq = nks >> 2;                           // k-steps of this wave: wave, wave + 4, ...
+    const int k0 = wave;
     const int kblocks = nks;
-    const uint16_t* b_src[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-        b_src[s2] = p.b + ((static_cast<int64_t>(e) * (p.N >> 5) + nb * 2 + s2) * kblocks + k0) * kFragElems +
-                    lane * 8;
+    // the workgroup's weights are one contiguous run; the four waves take every
+    // fourth k-step, so together they stream it front to back, 8 KiB per step
+    const uint16_t* b_src = p.b + frag_block(e, nb * 2, k0, p.N, kblocks) * kFragElems + lane * 8;
 
     // one row group: MT 32-row tiles starting at row g0 of the segment (MT = 1
     // when at most 32 rows remain, which is the usual case in decode)
@@ -395,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
             const int rr = g0 + t * 32 + (lane & 31);
             const int r = seg0 + (rr < rows ? rr : 0);
             const int64_t src = p.a_rows != nullptr ? p.a_rows[r] : r;
-            a_src[t] = p.a + src * p.Kd + static_cast<int64_t>(k0) * 16 + (lane >> 5) * 8;
+            a_src[t] = p.a + src * p.Kd + static_cast<int64_t>(k0) * 16 + (lane >> 5) * 8;   // step kc: + 64 kc
         }
         floatx16 acc[MT][2];
 #pragma unroll
@@ -408,26 +415,37 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
         u32x4 fb[BD][2], fa[BD][MT];
         auto load = [&](int slot, int kk) {       // k-step kk of this wave's range (clamped)
             const int kc = min(kk, kq - 1);
-            fb[slot][0] = *reinterpret_cast<const u32x4*>(b_src[0] + static_cast<int64_t>(kc) * kFragElems);
-            fb[slot][1] = *reinterpret_cast<const u32x4*>(b_src[1] + static_cast<int64_t>(kc) * kFragElems);
+            // weights are read once: non-temporal loads keep them from displacing
+            // the activation rows in the caches
+            const uint16_t* bk = b_src + static_cast<int64_t>(kc) * 8 * kFragElems;
+            fb[slot][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bk));
+            fb[slot][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bk + kFragElems));
 #pragma unroll
-            for (int t = 0; t < MT; ++t) fa[slot][t] = *reinterpret_cast<const u32x4*>(a_src[t] + kc * 16);
+            for (int t = 0; t < MT; ++t) fa[slot][t] = *reinterpret_cast<const u32x4*>(a_src[t] + kc * 64);
+        };
+        auto step = [&](int j) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                acc[t][0] = mfma32<F16>(fa[j][t], fb[j][0], acc[t][0]);
+                acc[t][1] = mfma32<F16>(fa[j][t], fb[j][1], acc[t][1]);
+            }
         };
 #pragma unroll
         for (int j = 0; j < BD; ++j) load(j, j);
-        for (int kb = 0; kb < kq; kb += BD) {
+        // whole turns of the ring with no branches inside, so that the wait before
+        // each step lets the younger BD-1 steps' loads stay in flight (a guarded
+        // step would make the compiler drain every load at the turn's start)
+        int kb = 0;
+        for (; kb + BD <= kq; kb += BD) {
 #pragma unroll
             for (int j = 0; j < BD; ++j) {
-                if (kb + j < kq) {                     // uniform
-#pragma unroll
-                    for (int t = 0; t < MT; ++t) {
-                        acc[t][0] = mfma32<F16>(fa[j][t], fb[j][0], acc[t][0]);
-                        acc[t][1] = mfma32<F16>(fa[j][t], fb[j][1], acc[t][1]);
-                    }
-                    load(j, kb + j + BD);
-                }
+                step(j);
+                load(j, kb + j + BD);
             }
         }
+#pragma unroll
+        for (int j = 0; j < BD; ++j)
+            if (kb + j < kq) step(j);                  // uniform
 
         // the four partial tiles go through LDS; each thread then adds the four
         // partials of 8 (row, column) pairs in wave order and applies the epilogue
@@ -510,7 +528,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const ST* __restrict_
     const int n32 = pcol >> 5;
     const int lanei = (pcol & 31) + 32 * (k8 & 1);
     const int k16 = k8 >> 1;
-    uint16_t* d = dst + ((static_cast<int64_t>(e) * (N >> 5) + n32) * (Kd >> 4) + k16) * kFragElems + lanei * 8;
+    uint16_t* d = dst + frag_block(e, n32, k16, N, Kd >> 4) * kFragElems + lanei * 8;
     u32x4 o;
     o[0] = v[0] | (static_cast<uint32_t>(v[1]) << 16);
     o[1] = v[2] | (static_cast<uint32_t>(v[3]) << 16);
