@@ -369,6 +369,13 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 template <int N> struct IntC { static constexpr int value = N; };
 
+// Raw buffer resource over the activation matrix (stride 0, byte-addressed):
+// offsets at or past kBufferRange load zeros.  The launcher keeps every valid
+// offset below kBufferRange.
+constexpr int kBufferRange = 0x7FFFFFFF;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kBufferFlags = 0x00020000;              // 32-bit data format, the usual gfx9 word 3
+
 template <int MODE, bool F16, int OUT, int BD>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p) {
     typedef typename OutType<OUT>::type OutT;
@@ -380,9 +387,6 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
     const int nblk = p.N >> 6;
     const int e = blockIdx.x / nblk;
     const int nb = blockIdx.x - e * nblk;
-    const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
-    const int rows = seg1 - seg0;
-    if (rows <= 0) return;                             // uniform over the workgroup
 
     const int nks = p.Kd >> 4;                         // k-steps (a multiple of 4)
     const int kq = nks >> 2;                           // k-steps of this wave: wave, wave + 4, ...
@@ -391,18 +395,45 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
     // the workgroup's weights are one contiguous run; the four waves take every
     // fourth k-step, so together they stream it front to back, 8 KiB per step
     const uint16_t* b_src = p.b + frag_block(e, nb * 2, k0, p.N, kblocks) * kFragElems + lane * 8;
+    u32x4 fb[BD][2];
+    auto load_b = [&](int slot, int kk) {              // k-step kk of this wave's range (clamped)
+        // weights are read once: non-temporal loads keep them from displacing
+        // the activation rows in the caches
+        const uint16_t* bk = b_src + static_cast<int64_t>(min(kk, kq - 1)) * 8 * kFragElems;
+        fb[slot][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bk));
+        fb[slot][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bk + kFragElems));
+    };
+    // the first ring of weight loads needs no routing data: it is in flight
+    // while the expert's row range and row indices are read
+#pragma unroll
+    for (int j = 0; j < BD; ++j) load_b(j, j);
+
+    const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
+    const int rows = seg1 - seg0;
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.a), 0, kBufferRange, kBufferFlags);
+    if (rows <= 0) {                                   // uniform over the workgroup
+        // consume the ring here too, so that its loads stay ahead of the branch
+#pragma unroll
+        for (int j = 0; j < BD; ++j) asm volatile("" ::"v"(fb[j][0]), "v"(fb[j][1]));
+        return;
+    }
 
     // one row group: MT 32-row tiles starting at row g0 of the segment (MT = 1
     // when at most 32 rows remain, which is the usual case in decode)
     auto group = [&](auto mt_tag, int g0) {
         constexpr int MT = decltype(mt_tag)::value;
-        const uint16_t* a_src[MT];
+        const bool first = g0 == 0;                    // its weight ring is already in flight
+        // activation rows through a buffer resource: lanes of rows past the
+        // segment get an offset past its range, so their loads return zeros
+        // without touching memory (a decode expert fills few of the 32 rows)
+        uint32_t a_off[MT];                            // bytes; step kc adds 128 kc
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             const int rr = g0 + t * 32 + (lane & 31);
             const int r = seg0 + (rr < rows ? rr : 0);
             const int64_t src = p.a_rows != nullptr ? p.a_rows[r] : r;
-            a_src[t] = p.a + src * p.Kd + static_cast<int64_t>(k0) * 16 + (lane >> 5) * 8;   // step kc: + 64 kc
+            a_off[t] = rr < rows ? static_cast<uint32_t>((src * p.Kd + k0 * 16 + (lane >> 5) * 8) * 2) : kOutOfRange;
         }
         floatx16 acc[MT][2];
 #pragma unroll
@@ -412,16 +443,13 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[t][j][v] = 0.0f;
 
-        u32x4 fb[BD][2], fa[BD][MT];
-        auto load = [&](int slot, int kk) {       // k-step kk of this wave's range (clamped)
+        u32x4 fa[BD][MT];
+        auto load_a = [&](int slot, int kk) {
             const int kc = min(kk, kq - 1);
-            // weights are read once: non-temporal loads keep them from displacing
-            // the activation rows in the caches
-            const uint16_t* bk = b_src + static_cast<int64_t>(kc) * 8 * kFragElems;
-            fb[slot][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bk));
-            fb[slot][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bk + kFragElems));
 #pragma unroll
-            for (int t = 0; t < MT; ++t) fa[slot][t] = *reinterpret_cast<const u32x4*>(a_src[t] + kc * 64);
+            for (int t = 0; t < MT; ++t)
+                fa[slot][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            a_rsrc, a_off[t] + static_cast<uint32_t>(kc) * 128, 0, 0));
         };
         auto step = [&](int j) {
 #pragma unroll
@@ -430,8 +458,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
                 acc[t][1] = mfma32<F16>(fa[j][t], fb[j][1], acc[t][1]);
             }
         };
+        if (!first) {
 #pragma unroll
-        for (int j = 0; j < BD; ++j) load(j, j);
+            for (int j = 0; j < BD; ++j) load_b(j, j);
+        }
+#pragma unroll
+        for (int j = 0; j < BD; ++j) load_a(j, j);
         // whole turns of the ring with no branches inside, so that the wait before
         // each step lets the younger BD-1 steps' loads stay in flight (a guarded
         // step would make the compiler drain every load at the turn's start)
@@ -440,7 +472,8 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < BD; ++j) {
                 step(j);
-                load(j, kb + j + BD);
+                load_b(j, kb + j + BD);
+                load_a(j, kb + j + BD);
             }
         }
 #pragma unroll
@@ -631,8 +664,11 @@ int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, cons
     args.E_loc = E_loc;
     args.I = s.I;
     // routed evenly, an expert receives T*K/E rows; at most 64 expected -> the
-    // weight-streaming kernel (it stays correct for any row count)
-    args.skinny = static_cast<int64_t>(s.T) * s.K <= static_cast<int64_t>(64) * s.E;
+    // weight-streaming kernel (it stays correct for any row count), provided its
+    // byte offsets into the activation matrix fit its buffer range
+    const int64_t a_rows_max = a_rows != nullptr ? s.T : max_rows;
+    const int64_t a_bytes = a_rows_max * (which == MOE_GEMM_GATE_UP ? s.H : s.I) * 2;
+    args.skinny = static_cast<int64_t>(s.T) * s.K <= static_cast<int64_t>(64) * s.E && a_bytes <= kBufferRange;
     if (which == MOE_GEMM_GATE_UP) {
         args.b = packed;
         args.N = 2 * s.I;
