@@ -928,14 +928,82 @@ __device__ __forceinline__ uint64_t group16_max_u64(uint64_t v) {
 // segment land on 16 distinct 4-bank groups.
 __device__ __forceinline__ int swz256r(int r, int c) { return c ^ (r & 15); }
 
+// Eight canonical chain steps of the exact kernel: acc = fma(x[j], w[j], acc)
+// for j = 0..7 in order, w[j] the bf16 halves of w0..w3 (low half first)
+// widened exactly.  The _fetch form also issues the next segment's three LDS
+// reads (weights at aw, token row at ax + OX) before the steps and waits for
+// them at its end, so the reads overlap the steps and no load is in flight
+// outside the block.
+#define MOE_EXACT_STEPS                                                                                        \
+    "v_lshlrev_b32 %[t], 16, %[w0]\n\t"                                                                       \
+    "v_fmac_f32 %[acc], %[a0], %[t]\n\t"                                                                      \
+    "v_and_b32 %[t], 0xffff0000, %[w0]\n\t"                                                                   \
+    "v_fmac_f32 %[acc], %[a1], %[t]\n\t"                                                                      \
+    "v_lshlrev_b32 %[t], 16, %[w1]\n\t"                                                                       \
+    "v_fmac_f32 %[acc], %[a2], %[t]\n\t"                                                                      \
+    "v_and_b32 %[t], 0xffff0000, %[w1]\n\t"                                                                   \
+    "v_fmac_f32 %[acc], %[a3], %[t]\n\t"                                                                      \
+    "v_lshlrev_b32 %[t], 16, %[w2]\n\t"                                                                       \
+    "v_fmac_f32 %[acc], %[a4], %[t]\n\t"                                                                      \
+    "v_and_b32 %[t], 0xffff0000, %[w2]\n\t"                                                                   \
+    "v_fmac_f32 %[acc], %[a5], %[t]\n\t"                                                                      \
+    "v_lshlrev_b32 %[t], 16, %[w3]\n\t"                                                                       \
+    "v_fmac_f32 %[acc], %[a6], %[t]\n\t"                                                                      \
+    "v_and_b32 %[t], 0xffff0000, %[w3]\n\t"                                                                   \
+    "v_fmac_f32 %[acc], %[a7], %[t]\n\t"
+
+template <int OX>
+__device__ __forceinline__ void exact_steps_fetch(float& acc, const u32x4& w, const floatx4& x0, const floatx4& x1,
+                                                  u32x4& nw, floatx4& nx0, floatx4& nx1, uint32_t aw, uint32_t ax) {
+    float t;
+    asm volatile("ds_read_b128 %[nw], %[aw]\n\t"
+                 "ds_read_b128 %[nx0], %[ax] offset:%[ox0]\n\t"
+                 "ds_read_b128 %[nx1], %[ax] offset:%[ox1]\n\t"
+                 MOE_EXACT_STEPS
+                 "s_waitcnt lgkmcnt(0)"
+                 : [acc] "+v"(acc), [nw] "=&v"(nw), [nx0] "=&v"(nx0), [nx1] "=&v"(nx1), [t] "=&v"(t)
+                 : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [a0] "v"(x0[0]),
+                   [a1] "v"(x0[1]), [a2] "v"(x0[2]), [a3] "v"(x0[3]), [a4] "v"(x1[0]), [a5] "v"(x1[1]),
+                   [a6] "v"(x1[2]), [a7] "v"(x1[3]), [aw] "v"(aw), [ax] "v"(ax), [ox0] "i"(OX), [ox1] "i"(OX + 16)
+                 : "memory");
+}
+
+__device__ __forceinline__ void exact_steps(float& acc, const u32x4& w, const floatx4& x0, const floatx4& x1) {
+    float t;
+    asm volatile(MOE_EXACT_STEPS
+                 : [acc] "+v"(acc), [t] "=&v"(t)
+                 : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [a0] "v"(x0[0]),
+                   [a1] "v"(x0[1]), [a2] "v"(x0[2]), [a3] "v"(x0[3]), [a4] "v"(x1[0]), [a5] "v"(x1[1]),
+                   [a6] "v"(x1[2]), [a7] "v"(x1[3]));
+}
+#undef MOE_EXACT_STEPS
+
+// Segments C .. NSEG-1 of one 128-h chunk of a chain (segment C's operands
+// already in registers); aw is the chain's weight row, ax its token row.
+template <int C, int NSEG>
+__device__ __forceinline__ void exact_chain_segments(float& a, u32x4 wv, floatx4 x0, floatx4 x1, uint32_t aw,
+                                                     int u, uint32_t ax) {
+    if constexpr (C + 1 < NSEG) {
+        u32x4 wn;
+        floatx4 y0, y1;
+        exact_steps_fetch<(8 * C + 8) * 4>(a, wv, x0, x1, wn, y0, y1, aw + swz256r(u, C + 1) * 16, ax);
+        exact_chain_segments<C + 1, NSEG>(a, wn, y0, y1, aw, u, ax);
+    } else {
+        exact_steps(a, wv, x0, x1);
+    }
+}
+
 // A workgroup owns BT = 4 * WAVES tokens; 16 lanes per token.  Lane s of a
-// token's group screens experts s, s+16, ..., s+112, then evaluates candidates
-// s, s+16, ... of the token's candidate list.  The canonical chains read
-// 128-h chunks of the transposed router-weight rows of the union of the
-// block's candidates and of the token rows, staged in LDS by a ring of
-// direct-to-LDS copies (NB stages); each wave widens its four token rows to
-// float32 once per chunk in a wave-private area, so a chain step costs one
-// widening of the weight and one fma.
+// token's group screens experts s, s+16, ..., s+112.  The candidate chains of
+// a wave's four tokens are then laid out one after another and dealt over all
+// 64 lanes (chain c to lane c % 64), so a token with more than 16 candidates
+// borrows lanes its neighbours leave idle instead of running a second round.
+// The canonical chains read 128-h chunks of the transposed router-weight rows
+// of the union of the block's candidates and of the token rows, staged in LDS
+// by a ring of direct-to-LDS copies (NB stages); each wave widens its four
+// token rows to float32 once per chunk in a wave-private area, so a chain step
+// costs one widening of the weight and one fma.  The finished logits go back
+// through LDS to the 16 lanes of their token, which select its top K.
 template <int WAVES, int NB, int SMAX>
 __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wT, const float* __restrict__ bias,
@@ -953,7 +1021,10 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
     constexpr int QMAX = (E / 4 + TROWS / 4 + WAVES - 1) / WAVES;   // copies per wave per chunk, at most
     __shared__ __attribute__((aligned(1024))) uint16_t s_ring[NB][STAGE];
     __shared__ __attribute__((aligned(16))) float s_xf[WAVES][4][HC + 4];
-    __shared__ uint8_t s_cand[WAVES][4][E];
+    __shared__ uint16_t s_chain[WAVES][4 * E];             // expert | (token of the wave << 8)
+    __shared__ uint16_t s_perm[WAVES][4 * E];              // chain dealt to slot j (lane j % 64)
+    __shared__ int s_hist[WAVES][16];
+    static_assert(STAGE * 2 >= WAVES * 4 * E * 4, "the first ring stage holds the finished chain sums");
     __shared__ int s_flag[E];
     __shared__ uint8_t s_map[E];
     __shared__ uint8_t s_list[E];
@@ -1036,12 +1107,17 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
         if (s >= d) incl += o;
     }
     const int total = __shfl(incl, 15, 16);      // candidates of this token
+    // the wave's chain list: token 0's candidates, then token 1's, ...
+    const int tot0 = __shfl(incl, 15, kWave), tot1 = __shfl(incl, 31, kWave);
+    const int tot2 = __shfl(incl, 47, kWave), tot3 = __shfl(incl, 63, kWave);
+    const int nwc = tot0 + tot1 + tot2 + tot3;   // chains of this wave (wave-uniform)
+    const int base = (g > 0 ? tot0 : 0) + (g > 1 ? tot1 : 0) + (g > 2 ? tot2 : 0);   // first chain of token g
     {
-        int pos = incl - mine;
+        int pos = base + incl - mine;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if ((cm >> i) & 1u) {
-                s_cand[wave][g][pos++] = static_cast<uint8_t>(s + 16 * i);
+                s_chain[wave][pos++] = static_cast<uint16_t>((s + 16 * i) | (g << 8));
                 s_flag[s + 16 * i] = 1;
             }
     }
@@ -1092,22 +1168,57 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
             if (j < q) dma16(src[j] + static_cast<int64_t>(kc) * HC, &s_ring[st][dst[j]]);
     };
 
-    // this lane's chains: candidates s + 16 p of its token
-    constexpr int PMAX = E / 16;
-    int urow[PMAX];
-    int eid[PMAX];
-    const int np = valid ? (total - s + 15) / 16 : 0;   // chains of this lane
+    // ---- deal the wave's chains to slots (slot j runs on lane j % 64, round
+    // j / 64).  A chain reads its union row in bank group (row index mod 16)
+    // (swz256r), and the 16 lanes of one LDS read pass conflict when two of them
+    // read different rows of one group.  So the chains are ordered by (rank
+    // within their group, group): any 16 consecutive slots then hold at most two
+    // chains of one group, and a full rank holds each group once. ----
+    constexpr int PMAX = 4 * E / kWave;
+    if (lane < 16) s_hist[wave][lane] = 0;
+    __syncthreads();
+    int rk[PMAX], rg[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
-        const int c = s + 16 * p;
-        eid[p] = c < total ? s_cand[wave][g][c] : 0;
-        urow[p] = c < total ? s_map[eid[p]] : 0;
+        const int c = lane + kWave * p;
+        rg[p] = c < nwc ? (s_map[s_chain[wave][c] & 0xFF] & 15) : 0;
+        rk[p] = c < nwc ? atomicAdd(&s_hist[wave][rg[p]], 1) : 0;
+    }
+    __syncthreads();
+    int cnt[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cnt[r] = s_hist[wave][r];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int c = lane + kWave * p;
+        if (c < nwc) {
+            int pos = 0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pos += min(cnt[r], rk[p]) + ((r < rg[p] && cnt[r] > rk[p]) ? 1 : 0);
+            s_perm[wave][pos] = static_cast<uint16_t>(c);
+        }
+    }
+    __syncthreads();
+
+    // this lane's chains: slots lane + 64 p (tokens past T have no candidates,
+    // so every slot below nwc is a real chain)
+    int urow[PMAX];
+    int xoff[PMAX];                               // float offset of the chain's token row in s_xf[wave]
+    int orig[PMAX];                               // the chain's place in the wave's list
+    const int np = (nwc - lane + kWave - 1) / kWave;   // chains of this lane
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int j = lane + kWave * p;
+        orig[p] = j < nwc ? s_perm[wave][j] : 0;
+        const int ent = j < nwc ? s_chain[wave][orig[p]] : 0;
+        urow[p] = j < nwc ? s_map[ent & 0xFF] : 0;
+        xoff[p] = (ent >> 8) * (HC + 4);
     }
     float acc[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) acc[p] = 0.0f;
     const int nc = H / HC;
-    const float* xw = s_xf[wave][g];
+    const float* xw0 = &s_xf[wave][0][0];
     const int xrow = XOFF + (wave * 4 + g) * RE;
 
 #pragma unroll
@@ -1133,45 +1244,39 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
                 // operands of segment c + 1 are read while segment c's fma chain runs
                 float a = acc[p];
                 const int u = urow[p];
+                const float* xw = xw0 + xoff[p];
                 const uint16_t* wr = sr + u * RE;
+                const uint32_t aw = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(wr));
+                const uint32_t ax = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(xw));
                 u32x4 wv = *reinterpret_cast<const u32x4*>(&wr[swz256r(u, 0) * 8]);
                 floatx4 x0 = *reinterpret_cast<const floatx4*>(&xw[0]);
                 floatx4 x1 = *reinterpret_cast<const floatx4*>(&xw[4]);
-#pragma unroll
-                for (int c = 0; c < HC / 8; ++c) {
-                    u32x4 wn;
-                    floatx4 y0, y1;
-                    if (c + 1 < HC / 8) {
-                        wn = *reinterpret_cast<const u32x4*>(&wr[swz256r(u, c + 1) * 8]);
-                        y0 = *reinterpret_cast<const floatx4*>(&xw[8 * c + 8]);
-                        y1 = *reinterpret_cast<const floatx4*>(&xw[8 * c + 12]);
-                    }
-                    a = fmaf(x0[0], bf_lo(wv[0]), a);
-                    a = fmaf(x0[1], bf_hi(wv[0]), a);
-                    a = fmaf(x0[2], bf_lo(wv[1]), a);
-                    a = fmaf(x0[3], bf_hi(wv[1]), a);
-                    a = fmaf(x1[0], bf_lo(wv[2]), a);
-                    a = fmaf(x1[1], bf_hi(wv[2]), a);
-                    a = fmaf(x1[2], bf_lo(wv[3]), a);
-                    a = fmaf(x1[3], bf_hi(wv[3]), a);
-                    if (c + 1 < HC / 8) {
-                        wv = wn;
-                        x0 = y0;
-                        x1 = y1;
-                    }
-                }
+                exact_chain_segments<0, HC / 8>(a, wv, x0, x1, aw, u, ax);
                 acc[p] = a;
             }
         }
     }
     wait_vmcnt<0>();
+    __syncthreads();   // every wave is done with the ring: it now holds the canonical chain sums
 
     // ---- select the top K of the candidates by canonical logit ----
-    uint64_t key[PMAX];
+    float* s_lg = reinterpret_cast<float*>(&s_ring[0][0]) + wave * 4 * E;
 #pragma unroll
-    for (int p = 0; p < PMAX; ++p) {
-        const float l = bias != nullptr ? acc[p] + bias[eid[p]] : acc[p];
-        key[p] = p < np ? make_key(l, eid[p]) : 0ull;
+    for (int p = 0; p < PMAX; ++p)
+        if (p < np) s_lg[orig[p]] = acc[p];
+    wait_lgkmcnt0();   // the wave reads back only its own list
+    constexpr int PTOK = E / 16;                  // candidates s + 16 q of the token, per lane
+    uint64_t key[PTOK];
+#pragma unroll
+    for (int q = 0; q < PTOK; ++q) {
+        const int c = s + 16 * q;
+        if (valid && c < total) {
+            const int e = s_chain[wave][base + c] & 0xFF;
+            const float a = s_lg[base + c];
+            key[q] = make_key(bias != nullptr ? a + bias[e] : a, e);
+        } else {
+            key[q] = 0ull;
+        }
     }
     int my_e[4] = {0, 0, 0, 0};
     float my_l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1179,11 +1284,11 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
     for (int r = 0; r < K; ++r) {
         uint64_t best = 0ull;
 #pragma unroll
-        for (int p = 0; p < PMAX; ++p) best = key[p] > best ? key[p] : best;
+        for (int q = 0; q < PTOK; ++q) best = key[q] > best ? key[q] : best;
         best = group16_max_u64(best);
 #pragma unroll
-        for (int p = 0; p < PMAX; ++p)
-            if (key[p] == best) key[p] = 0ull;
+        for (int q = 0; q < PTOK; ++q)
+            if (key[q] == best) key[q] = 0ull;
         const float l = key_logit(best);
         if (r == 0) l0 = l;
         sum += expf(l - l0);
