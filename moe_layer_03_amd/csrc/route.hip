@@ -930,38 +930,40 @@ __device__ __forceinline__ int swz256r(int r, int c) { return c ^ (r & 15); }
 
 // Eight canonical chain steps of the exact kernel: acc = fma(x[j], w[j], acc)
 // for j = 0..7 in order, w[j] the bf16 halves of w0..w3 (low half first)
-// widened exactly.  The _fetch form also issues the next segment's three LDS
+// widened exactly.  Each widening runs one step ahead into its own temporary,
+// so an fma waits only for the previous fma.  The _fetch form also issues the next segment's three LDS
 // reads (weights at aw, token row at ax + OX) before the steps and waits for
 // them at its end, so the reads overlap the steps and no load is in flight
 // outside the block.
 #define MOE_EXACT_STEPS                                                                                        \
-    "v_lshlrev_b32 %[t], 16, %[w0]\n\t"                                                                       \
-    "v_fmac_f32 %[acc], %[a0], %[t]\n\t"                                                                      \
-    "v_and_b32 %[t], 0xffff0000, %[w0]\n\t"                                                                   \
-    "v_fmac_f32 %[acc], %[a1], %[t]\n\t"                                                                      \
-    "v_lshlrev_b32 %[t], 16, %[w1]\n\t"                                                                       \
-    "v_fmac_f32 %[acc], %[a2], %[t]\n\t"                                                                      \
-    "v_and_b32 %[t], 0xffff0000, %[w1]\n\t"                                                                   \
-    "v_fmac_f32 %[acc], %[a3], %[t]\n\t"                                                                      \
-    "v_lshlrev_b32 %[t], 16, %[w2]\n\t"                                                                       \
-    "v_fmac_f32 %[acc], %[a4], %[t]\n\t"                                                                      \
-    "v_and_b32 %[t], 0xffff0000, %[w2]\n\t"                                                                   \
-    "v_fmac_f32 %[acc], %[a5], %[t]\n\t"                                                                      \
-    "v_lshlrev_b32 %[t], 16, %[w3]\n\t"                                                                       \
-    "v_fmac_f32 %[acc], %[a6], %[t]\n\t"                                                                      \
-    "v_and_b32 %[t], 0xffff0000, %[w3]\n\t"                                                                   \
-    "v_fmac_f32 %[acc], %[a7], %[t]\n\t"
+    "v_lshlrev_b32 %[t0], 16, %[w0]\n\t"                                                                      \
+    "v_and_b32 %[t1], 0xffff0000, %[w0]\n\t"                                                                  \
+    "v_fmac_f32 %[acc], %[a0], %[t0]\n\t"                                                                     \
+    "v_lshlrev_b32 %[t2], 16, %[w1]\n\t"                                                                      \
+    "v_fmac_f32 %[acc], %[a1], %[t1]\n\t"                                                                     \
+    "v_and_b32 %[t3], 0xffff0000, %[w1]\n\t"                                                                  \
+    "v_fmac_f32 %[acc], %[a2], %[t2]\n\t"                                                                     \
+    "v_lshlrev_b32 %[t0], 16, %[w2]\n\t"                                                                      \
+    "v_fmac_f32 %[acc], %[a3], %[t3]\n\t"                                                                     \
+    "v_and_b32 %[t1], 0xffff0000, %[w2]\n\t"                                                                  \
+    "v_fmac_f32 %[acc], %[a4], %[t0]\n\t"                                                                     \
+    "v_lshlrev_b32 %[t2], 16, %[w3]\n\t"                                                                      \
+    "v_fmac_f32 %[acc], %[a5], %[t1]\n\t"                                                                     \
+    "v_and_b32 %[t3], 0xffff0000, %[w3]\n\t"                                                                  \
+    "v_fmac_f32 %[acc], %[a6], %[t2]\n\t"                                                                     \
+    "v_fmac_f32 %[acc], %[a7], %[t3]\n\t"
 
 template <int OX>
 __device__ __forceinline__ void exact_steps_fetch(float& acc, const u32x4& w, const floatx4& x0, const floatx4& x1,
                                                   u32x4& nw, floatx4& nx0, floatx4& nx1, uint32_t aw, uint32_t ax) {
-    float t;
+    float t0, t1, t2, t3;
     asm volatile("ds_read_b128 %[nw], %[aw]\n\t"
                  "ds_read_b128 %[nx0], %[ax] offset:%[ox0]\n\t"
                  "ds_read_b128 %[nx1], %[ax] offset:%[ox1]\n\t"
                  MOE_EXACT_STEPS
                  "s_waitcnt lgkmcnt(0)"
-                 : [acc] "+v"(acc), [nw] "=&v"(nw), [nx0] "=&v"(nx0), [nx1] "=&v"(nx1), [t] "=&v"(t)
+                 : [acc] "+v"(acc), [nw] "=&v"(nw), [nx0] "=&v"(nx0), [nx1] "=&v"(nx1), [t0] "=&v"(t0),
+                   [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
                  : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [a0] "v"(x0[0]),
                    [a1] "v"(x0[1]), [a2] "v"(x0[2]), [a3] "v"(x0[3]), [a4] "v"(x1[0]), [a5] "v"(x1[1]),
                    [a6] "v"(x1[2]), [a7] "v"(x1[3]), [aw] "v"(aw), [ax] "v"(ax), [ox0] "i"(OX), [ox1] "i"(OX + 16)
@@ -969,9 +971,9 @@ __device__ __forceinline__ void exact_steps_fetch(float& acc, const u32x4& w, co
 }
 
 __device__ __forceinline__ void exact_steps(float& acc, const u32x4& w, const floatx4& x0, const floatx4& x1) {
-    float t;
+    float t0, t1, t2, t3;
     asm volatile(MOE_EXACT_STEPS
-                 : [acc] "+v"(acc), [t] "=&v"(t)
+                 : [acc] "+v"(acc), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
                  : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [a0] "v"(x0[0]),
                    [a1] "v"(x0[1]), [a2] "v"(x0[2]), [a3] "v"(x0[3]), [a4] "v"(x1[0]), [a5] "v"(x1[1]),
                    [a6] "v"(x1[2]), [a7] "v"(x1[3]));
