@@ -6,6 +6,7 @@
 #include <cstddef>
 
 #include "common.hpp"
+#include "route_prefetch.hpp"
 
 namespace moe {
 
@@ -226,8 +227,18 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
     int32_t* rs = row_slot ? row_slot : w.row_slot;
     int32_t* sr = slot_row ? slot_row : w.slot_row;
 
-    MOE_TRY(launch_route(*s, x, x_dtype, w_router, bias, idx, tw, nullptr, w.route_scratch, w.route_bytes, st));
     const uint16_t* pk = static_cast<const uint16_t*>(packed);
+    // Few rows per expert: the gate/up GEMM after routing streams its weights
+    // from HBM and the router leaves most CUs idle, so those CUs read the
+    // gate/up weights into the last-level cache meanwhile (when they fit).
+    CachePrefetch pf;
+    const size_t gu_bytes = packed_gate_up_elems(*s) * 2;
+    if (gemm_streams_weights(*s) && gu_bytes <= kLastLevelCacheBytes) {
+        pf.region = pk;
+        pf.bytes = gu_bytes;
+    }
+    MOE_TRY(launch_route_prefetch(*s, x, x_dtype, w_router, bias, idx, tw, nullptr, w.route_scratch, w.route_bytes,
+                                  st, pf));
     // bf16 layers multiply in bf16 (exact inputs) and the gate/up GEMM gathers
     // the token rows straight from x; float32 layers pack the rows as fp16
     // first.  The SwiGLU activations and expert outputs are fp16: rounding them

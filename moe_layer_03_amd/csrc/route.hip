@@ -17,6 +17,7 @@
 // dependent chain, with a deeper prefetch.  Larger E uses the generic kernel.  Selection happens in registers with wave-wide
 // 64-bit max reductions over (orderable logit, ~expert) keys.
 #include "common.hpp"
+#include "route_prefetch.hpp"
 
 #include <type_traits>
 #include <utility>
@@ -444,11 +445,39 @@ __device__ __forceinline__ void chain_fetch(floatx4& nx0, floatx4& nx1, float (&
 }
 #undef MOE_CHAIN_FETCH
 
+// Reads units [b*n/B, (b+1)*n/B) of a region of n 1 KiB units (workgroup b of
+// B) into a scratch KiB of LDS per wave, up to 32 copies in flight per wave,
+// and discards them: the bytes pass through the last-level cache, where a
+// kernel launched next finds them.  Every address stays inside the region
+// (the last group repeats the last unit); all copies land before return.
+constexpr int kCacheGroup = 16;   // copies issued per wave between waits
+__device__ void cache_region(const uint16_t* __restrict__ region, int64_t units, int b, int B,
+                             void* lds_scratch) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    const int64_t u0 = units * b / B, u1 = units * (b + 1) / B;
+    uint16_t* dst = static_cast<uint16_t*>(lds_scratch) + wave * 512;
+    int64_t u = u0 + wave;
+    const int64_t step = static_cast<int64_t>(nw) * kCacheGroup;
+    bool first = true;
+    for (; u < u1; u += step) {
+#pragma unroll
+        for (int j = 0; j < kCacheGroup; ++j) {
+            const int64_t v = min(u + static_cast<int64_t>(j) * nw, u1 - 1);
+            dma16(region + v * 512 + lane * 8, dst);
+        }
+        if (!first) wait_vmcnt<kCacheGroup>();   // the previous group has landed
+        first = false;
+    }
+    wait_vmcnt<0>();
+}
+
 template <typename XT, int TPW, int WE, int DW, int HC, int NB, int XMAX>
 __global__ __launch_bounds__((TPW * WE + DW) * 64) void route_chain_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias,
     int T, int H, int E, int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, int nroute, const uint16_t* __restrict__ pf, int64_t pf_units) {
     constexpr bool BF16 = sizeof(XT) == 2;
     constexpr int CW = TPW * WE;                              // chain waves
     constexpr int CT = CW * 64;                               // chain threads
@@ -471,6 +500,12 @@ __global__ __launch_bounds__((TPW * WE + DW) * 64) void route_chain_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (static_cast<int>(blockIdx.x) >= nroute) {
+        // workgroups past the routing ones read a region the next kernel streams
+        // (the expert weights) so that it is in the last-level cache by then
+        cache_region(pf, pf_units, blockIdx.x - nroute, gridDim.x - nroute, &s_w[0][0]);
+        return;
+    }
     const int tok0 = blockIdx.x * TPW;
     const int nc = H / HC;
     float acc = 0.0f;
@@ -638,20 +673,31 @@ void launch_fast(const moe_shape& s, const XT* x, const XT* w, const float* bias
 
 template <typename XT, int TPW, int WE, int DW, int HC, int NB, int XMAX>
 void launch_chain(const moe_shape& s, const XT* x, const XT* w, const float* bias, int32_t* idx, float* tw,
-                  float* logits, hipStream_t st) {
+                  float* logits, const CachePrefetch& pf, hipStream_t st) {
     const int grid = (s.T + TPW - 1) / TPW;
-    hipLaunchKernelGGL((route_chain_kernel<XT, TPW, WE, DW, HC, NB, XMAX>), dim3(grid), dim3((TPW * WE + DW) * 64),
-                       0, st, x, w, bias, s.T, s.H, s.E, s.K, idx, tw, logits);
+    // spare CUs read the prefetch region while the routing workgroups run
+    int extra = 0;
+    if (pf.region != nullptr && pf.bytes >= 1024) {
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            int v = 0;
+            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+        }
+        if (grid < cus) extra = cus - grid;
+    }
+    hipLaunchKernelGGL((route_chain_kernel<XT, TPW, WE, DW, HC, NB, XMAX>), dim3(grid + extra),
+                       dim3((TPW * WE + DW) * 64), 0, st, x, w, bias, s.T, s.H, s.E, s.K, idx, tw, logits, grid,
+                       static_cast<const uint16_t*>(pf.region), static_cast<int64_t>(pf.bytes / 1024));
 }
 
 template <typename XT>
 void launch_route_dt(const moe_shape& s, const XT* x, const XT* w, const float* bias, int32_t* idx,
-                     float* tw, float* logits, hipStream_t st) {
+                     float* tw, float* logits, const CachePrefetch& pf, hipStream_t st) {
     // rows of the router weight must split into 16-byte pieces (E a multiple of 8 for bf16, 4 for float32)
     if (s.E <= 128 && s.E % (16 / sizeof(XT)) == 0 && s.T <= kChainMaxT && s.H <= 4096) {
         // one token per workgroup: chains spread over as many CUs as there are tokens
-        if (s.E <= 64) launch_chain<XT, 1, 1, 1, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, st);
-        else launch_chain<XT, 1, 2, 2, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, st);
+        if (s.E <= 64) launch_chain<XT, 1, 1, 1, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, pf, st);
+        else launch_chain<XT, 1, 2, 2, 64, 4, 4096>(s, x, w, bias, idx, tw, logits, pf, st);
         return;
     }
     if (s.E <= 128) {
@@ -1364,16 +1410,23 @@ size_t route_screen_bytes(const moe_shape& s, int x_dtype, int w_dtype) {
 
 int launch_route(const moe_shape& s, const void* x, int x_dtype, const void* w, const float* bias,
                  int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes, hipStream_t st) {
+    return launch_route_prefetch(s, x, x_dtype, w, bias, topk_idx, topk_w, logits, ws, ws_bytes, st,
+                                 CachePrefetch());
+}
+
+int launch_route_prefetch(const moe_shape& s, const void* x, int x_dtype, const void* w, const float* bias,
+                          int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
+                          hipStream_t st, CachePrefetch pf) {
     const size_t need = route_screen_bytes(s, x_dtype, x_dtype);
     if (logits == nullptr && ws != nullptr && need > 0 && ws_bytes >= need)
         launch_route_screened(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias, topk_idx,
                               topk_w, ws, st);
     else if (x_dtype == MOE_BF16)
         launch_route_dt<uint16_t>(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
-                                  topk_idx, topk_w, logits, st);
+                                  topk_idx, topk_w, logits, pf, st);
     else
         launch_route_dt<float>(s, static_cast<const float*>(x), static_cast<const float*>(w), bias, topk_idx,
-                               topk_w, logits, st);
+                               topk_w, logits, pf, st);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
