@@ -100,3 +100,31 @@ def test_layer_full_size(name):
     counts = d["counts"]
     print(f"[{name}] N_loc={int(d['offsets'][-1])} counts min/mean/max={counts.min()}/{counts.mean():.1f}/"
           f"{counts.max()}", flush=True)
+
+
+STAGED = [W.WORKLOADS["tiny"], W.Workload("small_batch", T=96, H=512, E=64, K=8, I=256, e_begin=0, e_end=8,
+                                             dtype="bf16")] + MID[:2]
+
+
+@pytest.mark.parametrize("wl", STAGED, ids=lambda w: w.name)
+def test_fused_layer_equals_staged_calls(wl):
+    """The fused entry point (which, for small batches, also reads the gate/up
+    weights into the last-level cache while routing) and the staged entry
+    points in the same order give the same bits."""
+    layer = GpuLayer(W.make_inputs(wl))
+    fused = layer.run()
+    B, s, dev = layer.B, layer.s, layer.x.device
+    idx, tw, _ = B.moe_route(s, layer.x, layer.w_router, layer.bias)
+    d = B.moe_dispatch(s, idx, None if wl.dtype == "bf16" else layer.x,
+                       ws=torch.empty(max(B.moe_dispatch_workspace_bytes(s), 16), dtype=torch.uint8, device=dev))
+    if wl.dtype == "bf16":
+        h = B.moe_grouped_gemm(s, layer.x, d["offsets"], layer.packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_SWIGLU,
+                               a_rows=d["row_token"])
+    else:
+        h = B.moe_grouped_gemm(s, d["x_packed"], d["offsets"], layer.packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_SWIGLU)
+    y = B.moe_grouped_gemm(s, h, d["offsets"], layer.packed, B.MOE_GEMM_DOWN, B.MOE_EPI_NONE)
+    out = B.moe_combine(s, y, d["slot_row"], tw)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), fused["topk_idx"])
+    assert np.array_equal(d["slot_row"].cpu().numpy(), fused["slot_row"])
+    assert np.array_equal(out.cpu().numpy(), fused["out"]), "fused and staged outputs differ"
