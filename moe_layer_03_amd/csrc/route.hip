@@ -1385,8 +1385,10 @@ void launch_route_screened(const moe_shape& s, const uint16_t* x, const uint16_t
     else launch_screen<1>(s, x, w, ws, S, st);
     // the exact kernel sums SMAX >= S slice partials (screen_slices gives S <= 16)
     if (s.T >= 2048) {
-        if (S <= 4) launch_exact<8, 3, 4>(s, x, bias, ws, S, idx, tw, st);
-        else launch_exact<8, 3, 16>(s, x, bias, ws, S, idx, tw, st);
+        // 6 waves, 24 tokens per workgroup: one workgroup per CU (LDS), and 6000
+        // tokens make 250 of them, nearly one per CU of the 256
+        if (S <= 4) launch_exact<6, 3, 4>(s, x, bias, ws, S, idx, tw, st);
+        else launch_exact<6, 3, 16>(s, x, bias, ws, S, idx, tw, st);
     } else {
         launch_exact<4, 3, 16>(s, x, bias, ws, S, idx, tw, st);
     }
