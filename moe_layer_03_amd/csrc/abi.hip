@@ -233,7 +233,7 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
     // gate/up weights into the last-level cache meanwhile (when they fit).
     CachePrefetch pf;
     const size_t gu_bytes = packed_gate_up_elems(*s) * 2;
-    if (gemm_streams_weights(*s) && gu_bytes <= kLastLevelCacheBytes) {
+    if (gemm_streams_weights(*s, MOE_GEMM_GATE_UP, x_dtype == MOE_BF16) && gu_bytes <= kLastLevelCacheBytes) {
         pf.region = pk;
         pf.bytes = gu_bytes;
     }
@@ -245,7 +245,12 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
     // to bf16 instead would cost about 2% of the output RMS in the largest
     // elements.
     const int op = gate_up_operand_dtype(x_dtype);
-    if (x_dtype == MOE_BF16) {
+    if (x_dtype == MOE_BF16 && gemm_can_derive_dispatch(*s)) {
+        // few rows per expert: the weight-streaming gate/up GEMM derives the
+        // dispatch itself (one launch fewer) and writes its outputs on the way
+        MOE_TRY(launch_gate_up_deriving_dispatch(*s, static_cast<const uint16_t*>(x), idx, pk, w.h, cnt, off, rt, rs,
+                                                 sr, st));
+    } else if (x_dtype == MOE_BF16) {
         MOE_TRY(launch_dispatch(*s, idx, nullptr, x_dtype, cnt, off, rt, rs, sr, nullptr, w.dispatch_scratch, st));
         MOE_TRY(launch_grouped_gemm(*s, static_cast<const uint16_t*>(x), op, rt, off, pk, MOE_GEMM_GATE_UP,
                                     MOE_EPI_SWIGLU, w.h, MOE_F16, st));

@@ -130,6 +130,19 @@ inline int gate_up_operand_dtype(int weight_dtype) { return weight_dtype == MOE_
 int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, const int32_t* a_rows,
                         const int32_t* offsets, const uint16_t* packed, int which, int epilogue, void* c,
                         int c_dtype, hipStream_t st);
+// Whether launch_grouped_gemm takes its weight-streaming form (few rows per
+// expert); gather: the rows are read through a row-to-token map.
+bool gemm_streams_weights(const moe_shape& s, int which, bool gather);
+// Whether the gate/up launch below applies (bf16 rows gathered from x, weight
+// streaming, at most 1024 tokens and 1024 local experts).
+bool gemm_can_derive_dispatch(const moe_shape& s);
+// Weight-streaming gate/up GEMM with the SwiGLU epilogue (fp16 h) that derives
+// the dispatch from topk_idx itself and writes the dispatch outputs (counts,
+// offsets, row_token, row_slot, slot_row) on the way: dispatch and gate/up in
+// one launch.
+int launch_gate_up_deriving_dispatch(const moe_shape& s, const uint16_t* x, const int32_t* topk_idx,
+                                     const uint16_t* packed, uint16_t* h, int32_t* counts, int32_t* offsets,
+                                     int32_t* row_token, int32_t* row_slot, int32_t* slot_row, hipStream_t st);
 
 int launch_combine(const moe_shape& s, const void* y_packed, int y_dtype, const int32_t* slot_row,
                    const float* topk_w, float* out, hipStream_t st);

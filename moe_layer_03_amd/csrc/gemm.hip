@@ -86,7 +86,19 @@ struct GemmArgs {
     int ldc;                   // output row stride (elements)
     int I;                     // intermediate size (gate/up column remap)
     int skinny;                // few rows per expert expected: weight-streaming kernel
+    // weight-streaming gate/up only, optional: derive the dispatch from the
+    // routing instead of reading offsets / a_rows (a holds the unpacked rows)
+    const int32_t* topk_idx;   // [T][K] expert ids, NULL: not derived
+    int e_begin, T, K;
+    int32_t* d_counts;         // dispatch outputs, written by each expert's first column block
+    int32_t* d_offsets;
+    int32_t* d_row_token;
+    int32_t* d_row_slot;
+    int32_t* d_slot_row;
 };
+
+constexpr int kDeriveMaxT = 1024;      // tokens of a derived dispatch (one expert's row list in LDS)
+constexpr int kDeriveMaxE = 1024;
 
 __device__ __forceinline__ int swz(int row, int kg) {
     // Swizzled granule position of logical granule kg (0..3) of a 64-byte row.
@@ -376,6 +388,78 @@ constexpr int kBufferRange = 0x7FFFFFFF;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kBufferFlags = 0x00020000;              // 32-bit data format, the usual gfx9 word 3
 
+// Sum of v over the 256 threads of the workgroup (uniform result).
+__device__ __forceinline__ int block_sum256(int v, int* s_w4) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    __syncthreads();                                   // s_w4 free
+    if ((threadIdx.x & (kWave - 1)) == 0) s_w4[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return s_w4[0] + s_w4[1] + s_w4[2] + s_w4[3];
+}
+
+// The dispatch of expert e derived in the workgroup from the routing: the
+// histogram of local experts gives the expert's first row (the exclusive sum
+// over the experts before it) and row count, and an order-keeping compaction of
+// the (token, slot) entries routed to e lists its rows by ascending token (a
+// token lists an expert once), the stable order of the dispatch.  The first
+// column block of every expert writes that expert's part of the dispatch
+// outputs; expert 0's also writes the total and -1 for non-local slots.
+__device__ void derive_dispatch(const GemmArgs& p, int e, int nb, int* s_cnt, int* s_list, int* s_w4, int& seg0,
+                                int& rows) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid >> 6;
+    for (int i = tid; i < p.E_loc; i += 256) s_cnt[i] = 0;
+    __syncthreads();
+    const int n = p.T * p.K;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int run = 0;                                       // entries of e listed so far (uniform)
+    for (int base = 0; base < n; base += 256) {
+        const int i = base + tid;
+        int v = -1;
+        if (i < n) {
+            v = p.topk_idx[i] - p.e_begin;
+            if (v >= 0 && v < p.E_loc) atomicAdd(&s_cnt[v], 1);
+        }
+        const bool mine = v == e;
+        const uint64_t m = __ballot(mine);
+        if (lane == 0) s_w4[wave] = __popcll(m);
+        __syncthreads();
+        int wb = 0;
+        for (int w = 0; w < wave; ++w) wb += s_w4[w];
+        const int tot = s_w4[0] + s_w4[1] + s_w4[2] + s_w4[3];
+        if (mine) s_list[run + wb + __popcll(m & below)] = i;
+        run += tot;
+        __syncthreads();                               // s_w4 reuse
+    }
+    rows = s_cnt[e];
+    int part = 0;
+    for (int k = tid; k < e; k += 256) part += s_cnt[k];
+    seg0 = block_sum256(part, s_w4);
+    if (nb != 0) return;
+    if (tid == 0) {
+        p.d_counts[e] = rows;
+        p.d_offsets[e] = seg0;
+    }
+    for (int r = tid; r < rows; r += 256) {
+        const int i = s_list[r];
+        const int t = i / p.K;
+        p.d_row_token[seg0 + r] = t;
+        p.d_row_slot[seg0 + r] = i - t * p.K;
+        p.d_slot_row[i] = seg0 + r;
+    }
+    if (e == 0) {
+        int all = 0;
+        for (int k = tid; k < p.E_loc; k += 256) all += s_cnt[k];
+        all = block_sum256(all, s_w4);
+        if (tid == 0) p.d_offsets[p.E_loc] = all;
+        for (int i = tid; i < n; i += 256) {
+            const int v = p.topk_idx[i] - p.e_begin;
+            if (v < 0 || v >= p.E_loc) p.d_slot_row[i] = -1;
+        }
+    }
+}
+
 template <int MODE, bool F16, int OUT, int BD>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p) {
     typedef typename OutType<OUT>::type OutT;
@@ -408,8 +492,17 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
 #pragma unroll
     for (int j = 0; j < BD; ++j) load_b(j, j);
 
-    const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
-    const int rows = seg1 - seg0;
+    __shared__ int s_cnt[kDeriveMaxE];
+    __shared__ int s_list[kDeriveMaxT];
+    __shared__ int s_w4[4];
+    const bool derived = p.topk_idx != nullptr;        // uniform
+    int seg0, rows;
+    if (derived) {
+        derive_dispatch(p, e, nb, s_cnt, s_list, s_w4, seg0, rows);
+    } else {
+        seg0 = p.offsets[e];
+        rows = p.offsets[e + 1] - seg0;
+    }
     const __amdgpu_buffer_rsrc_t a_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.a), 0, kBufferRange, kBufferFlags);
     if (rows <= 0) {                                   // uniform over the workgroup
@@ -432,7 +525,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p)
         for (int t = 0; t < MT; ++t) {
             const int rr = g0 + t * 32 + (lane & 31);
             const int r = seg0 + (rr < rows ? rr : 0);
-            const int64_t src = p.a_rows != nullptr ? p.a_rows[r] : r;
+            const int64_t src = derived ? s_list[rr < rows ? rr : 0] / p.K : (p.a_rows != nullptr ? p.a_rows[r] : r);
             a_off[t] = rr < rows ? static_cast<uint32_t>((src * p.Kd + k0 * 16 + (lane >> 5) * 8) * 2) : kOutOfRange;
         }
         floatx16 acc[MT][2];
@@ -651,12 +744,52 @@ int launch_pack_weights(const moe_shape& s, const void* w_gate, const void* w_up
     return MOE_OK;
 }
 
+bool gemm_streams_weights(const moe_shape& s, int which, bool gather) {
+    // routed evenly, an expert receives T*K/E rows; at most 64 expected -> the
+    // weight-streaming kernel (it stays correct for any row count), provided its
+    // byte offsets into the activation matrix fit its buffer range
+    const int E_loc = s.e_end - s.e_begin;
+    const int64_t max_rows = static_cast<int64_t>(s.T) * (s.K < E_loc ? s.K : E_loc);
+    const int64_t a_rows_max = gather ? s.T : max_rows;
+    const int64_t a_bytes = a_rows_max * (which == MOE_GEMM_GATE_UP ? s.H : s.I) * 2;
+    return static_cast<int64_t>(s.T) * s.K <= static_cast<int64_t>(64) * s.E && a_bytes <= kBufferRange;
+}
+
+bool gemm_can_derive_dispatch(const moe_shape& s) {
+    return gemm_streams_weights(s, MOE_GEMM_GATE_UP, true) && s.T <= kDeriveMaxT && s.e_end - s.e_begin <= kDeriveMaxE;
+}
+
+int launch_gate_up_deriving_dispatch(const moe_shape& s, const uint16_t* x, const int32_t* topk_idx,
+                                     const uint16_t* packed, uint16_t* h, int32_t* counts, int32_t* offsets,
+                                     int32_t* row_token, int32_t* row_slot, int32_t* slot_row, hipStream_t st) {
+    GemmArgs args{};
+    args.a = x;
+    args.b = packed;
+    args.c = h;
+    args.E_loc = s.e_end - s.e_begin;
+    args.I = s.I;
+    args.N = 2 * s.I;
+    args.Kd = s.H;
+    args.ldc = s.I;
+    args.skinny = 1;
+    args.topk_idx = topk_idx;
+    args.e_begin = s.e_begin;
+    args.T = s.T;
+    args.K = s.K;
+    args.d_counts = counts;
+    args.d_offsets = offsets;
+    args.d_row_token = row_token;
+    args.d_row_slot = row_slot;
+    args.d_slot_row = slot_row;
+    return launch_skinny<kSwiGLU, false, kOutF16>(args, st);
+}
+
 int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, const int32_t* a_rows,
                         const int32_t* offsets, const uint16_t* packed, int which, int epilogue, void* c, int c_dtype,
                         hipStream_t st) {
     const int E_loc = s.e_end - s.e_begin;
     const int max_rows = s.T * (s.K < E_loc ? s.K : E_loc);
-    GemmArgs args;
+    GemmArgs args{};
     args.a = a;
     args.a_rows = a_rows;
     args.offsets = offsets;
@@ -666,9 +799,7 @@ int launch_grouped_gemm(const moe_shape& s, const uint16_t* a, int a_dtype, cons
     // routed evenly, an expert receives T*K/E rows; at most 64 expected -> the
     // weight-streaming kernel (it stays correct for any row count), provided its
     // byte offsets into the activation matrix fit its buffer range
-    const int64_t a_rows_max = a_rows != nullptr ? s.T : max_rows;
-    const int64_t a_bytes = a_rows_max * (which == MOE_GEMM_GATE_UP ? s.H : s.I) * 2;
-    args.skinny = static_cast<int64_t>(s.T) * s.K <= static_cast<int64_t>(64) * s.E && a_bytes <= kBufferRange;
+    args.skinny = gemm_streams_weights(s, which, a_rows != nullptr);
     if (which == MOE_GEMM_GATE_UP) {
         args.b = packed;
         args.N = 2 * s.I;

@@ -16,14 +16,6 @@ struct CachePrefetch {
 // MI355X's last-level (Infinity) cache: regions larger than this are not prefetched.
 constexpr size_t kLastLevelCacheBytes = static_cast<size_t>(256) << 20;
 
-// Whether the grouped GEMMs take their weight-streaming form: an evenly routed
-// expert receives at most 64 rows (T*K <= 64*E), the same rule the GEMM
-// launcher applies.  Only a hint for prefetching: a mismatch costs time, never
-// a result.
-inline bool gemm_streams_weights(const moe_shape& s) {
-    return static_cast<int64_t>(s.T) * s.K <= static_cast<int64_t>(64) * s.E;
-}
-
 // launch_route, with the small-batch router's spare CUs reading pf meanwhile
 // (other router kernels ignore pf).
 int launch_route_prefetch(const moe_shape& s, const void* x, int x_dtype, const void* w, const float* bias,
