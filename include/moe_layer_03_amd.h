@@ -212,6 +212,12 @@ int moe_combine(const moe_shape* s, const void* y_packed, int y_dtype, const int
  *   bf16 layers read the token rows straight from x (no packed copy);
  *   float32 layers pack them as fp16 first; SwiGLU activations and expert
  *   outputs are fp16.
+ *   Small batches (an evenly routed expert gets at most 64 rows): while the
+ *   router runs, CUs it leaves idle read the gate/up weights into the
+ *   last-level cache; for bf16 layers of at most 1024 tokens the gate/up GEMM
+ *   also derives the dispatch itself (no separate dispatch launch).  Every
+ *   output is the same, to the bit, as the staged calls moe_route,
+ *   moe_dispatch, moe_grouped_gemm (gate/up, then down) and moe_combine.
  */
 int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
               const float* bias, const void* packed, float* out,
