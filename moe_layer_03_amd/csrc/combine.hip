@@ -9,7 +9,9 @@
 // entries (at most K rows), adds w * y_row in ascending slot order in float32
 // and writes the whole output row once -- no atomics, deterministic.  Each
 // thread handles 8 consecutive features: one 16-byte bf16/fp16 load (or two
-// 16-byte float32 loads) per slot, two 16-byte float32 stores.
+// 16-byte float32 loads) per slot, two 16-byte float32 stores.  Small batches
+// give each workgroup one token and half of its features, so a few hundred
+// tokens still spread over the chip.
 #include "common.hpp"
 
 namespace moe {
@@ -18,15 +20,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTokensPerBlock = 2;
 
-template <typename YT, bool F16>
+template <typename YT, bool F16, int TPB>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict__ y, int T, int H, int K,
                                                            const int32_t* __restrict__ slot_row,
                                                            const float* __restrict__ topk_w,
                                                            float* __restrict__ out) {
-    for (int q = 0; q < kTokensPerBlock; ++q) {
-        const int t = blockIdx.x * kTokensPerBlock + q;
+    // workgroup (x, y): tokens x*TPB .. +TPB-1, features y*CW .. +CW-1
+    const int cw = (H + gridDim.y - 1) / gridDim.y;
+    const int k_end = min(H, (static_cast<int>(blockIdx.y) + 1) * cw);
+    for (int q = 0; q < TPB; ++q) {
+        const int t = blockIdx.x * TPB + q;
         if (t >= T) return;
-        for (int k = threadIdx.x * 8; k < H; k += kThreads * 8) {
+        for (int k = blockIdx.y * cw + threadIdx.x * 8; k < k_end; k += kThreads * 8) {
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int j = 0; j < K; ++j) {
                 const int r = slot_row[static_cast<int64_t>(t) * K + j];
@@ -68,16 +73,35 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict_
 
 int launch_combine(const moe_shape& s, const void* y_packed, int y_dtype, const int32_t* slot_row,
                    const float* topk_w, float* out, hipStream_t st) {
-    const int grid = (s.T + kTokensPerBlock - 1) / kTokensPerBlock;
-    if (y_dtype == MOE_BF16)
-        hipLaunchKernelGGL((combine_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, st,
-                           static_cast<const uint16_t*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
-    else if (y_dtype == MOE_F16)
-        hipLaunchKernelGGL((combine_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, st,
-                           static_cast<const uint16_t*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
-    else
-        hipLaunchKernelGGL((combine_kernel<float, false>), dim3(grid), dim3(kThreads), 0, st,
-                           static_cast<const float*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+    // small batches: one token per workgroup and the features split in two, so
+    // that even a few hundred tokens spread over the chip; large batches: two
+    // tokens per workgroup, whole rows
+    const bool small = s.T < 2048;
+    const int tpb = small ? 1 : kTokensPerBlock;
+    const int ysplit = (small && s.H % (2 * kThreads * 8) == 0) ? 2 : 1;   // each half a whole number of passes
+    const dim3 grid((s.T + tpb - 1) / tpb, ysplit);
+    if (y_dtype == MOE_BF16) {
+        if (small)
+            hipLaunchKernelGGL((combine_kernel<uint16_t, false, 1>), grid, dim3(kThreads), 0, st,
+                               static_cast<const uint16_t*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+        else
+            hipLaunchKernelGGL((combine_kernel<uint16_t, false, kTokensPerBlock>), grid, dim3(kThreads), 0, st,
+                               static_cast<const uint16_t*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+    } else if (y_dtype == MOE_F16) {
+        if (small)
+            hipLaunchKernelGGL((combine_kernel<uint16_t, true, 1>), grid, dim3(kThreads), 0, st,
+                               static_cast<const uint16_t*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+        else
+            hipLaunchKernelGGL((combine_kernel<uint16_t, true, kTokensPerBlock>), grid, dim3(kThreads), 0, st,
+                               static_cast<const uint16_t*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+    } else {
+        if (small)
+            hipLaunchKernelGGL((combine_kernel<float, false, 1>), grid, dim3(kThreads), 0, st,
+                               static_cast<const float*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+        else
+            hipLaunchKernelGGL((combine_kernel<float, false, kTokensPerBlock>), grid, dim3(kThreads), 0, st,
+                               static_cast<const float*>(y_packed), s.T, s.H, s.K, slot_row, topk_w, out);
+    }
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
