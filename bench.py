@@ -35,8 +35,10 @@ def parse():
     from moe_layer_03_amd.workloads import WORKLOAD_ORDER
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the clocks settle only after a few tens of steps: with 5 warm-up steps the first timed region ran
+    # 4-7 % slower than with 30
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="prefill_ep4_shard", choices=WORKLOAD_ORDER)
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
