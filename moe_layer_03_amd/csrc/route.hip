@@ -1385,10 +1385,27 @@ void launch_route_screened(const moe_shape& s, const uint16_t* x, const uint16_t
     else launch_screen<1>(s, x, w, ws, S, st);
     // the exact kernel sums SMAX >= S slice partials (screen_slices gives S <= 16)
     if (s.T >= 2048) {
-        // 6 waves, 24 tokens per workgroup: one workgroup per CU (LDS), and 6000
-        // tokens make 250 of them, nearly one per CU of the 256
-        if (S <= 4) launch_exact<6, 3, 4>(s, x, bias, ws, S, idx, tw, st);
-        else launch_exact<6, 3, 16>(s, x, bias, ws, S, idx, tw, st);
+        // One workgroup fits a CU (LDS) and the chain steps are bound by the CU's
+        // LDS, so a launch costs about (rounds of workgroups over the CUs) x (waves
+        // per workgroup): 6 waves (24 tokens) when that fills the chip in fewer
+        // rounds -- 6000 tokens make 250 workgroups, one round -- else 8 waves
+        // (16384 tokens: 512 workgroups, two rounds, against three at 6 waves).
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            int v = 0;
+            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+        }
+        auto cost = [&](int waves) {
+            const int64_t wgs = (static_cast<int64_t>(s.T) + 4 * waves - 1) / (4 * waves);
+            return ((wgs + cus - 1) / cus) * waves;
+        };
+        if (cost(6) < cost(8)) {
+            if (S <= 4) launch_exact<6, 3, 4>(s, x, bias, ws, S, idx, tw, st);
+            else launch_exact<6, 3, 16>(s, x, bias, ws, S, idx, tw, st);
+        } else {
+            if (S <= 4) launch_exact<8, 3, 4>(s, x, bias, ws, S, idx, tw, st);
+            else launch_exact<8, 3, 16>(s, x, bias, ws, S, idx, tw, st);
+        }
     } else {
         launch_exact<4, 3, 16>(s, x, bias, ws, S, idx, tw, st);
     }
