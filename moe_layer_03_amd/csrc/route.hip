@@ -772,13 +772,14 @@ __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v <<
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 // Slices of H for the screening kernel: enough workgroups to cover the chip,
+// and while there are fewer than 4 slices, enough for two per CU (two fit);
 // every slice a whole number of chunks.
 __host__ __device__ inline int screen_tokens_per_block(int T) { return T >= 2048 ? 64 : 32; }
 inline int screen_slices(int T, int H) {
     const int nblk = (T + screen_tokens_per_block(T) - 1) / screen_tokens_per_block(T);
     const int chunks = H / kScrHC;
     int S = 1;
-    while (nblk * S < 256 && S < 16 && chunks % (2 * S) == 0) S *= 2;
+    while ((nblk * S < 256 || (nblk * S < 512 && S < 4)) && S < 16 && chunks % (2 * S) == 0) S *= 2;
     return S;
 }
 
