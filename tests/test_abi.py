@@ -131,3 +131,14 @@ def test_status_strings():
     for st in (B.MOE_OK, B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE, B.MOE_ERR_HIP):
         assert B.status_string(st).startswith("MOE_")
     assert B.status_string(12345) == "unknown status"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for several it exits with status 2 and says why."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
