@@ -36,6 +36,10 @@
 //     and the once-per-stage barrier sits between a stage's two k-steps, so it
 //     waits while MFMAs are still executing and every stage starts with its
 //     operands already in registers;
+//   * the k-loop is instantiated per count of active 32-row groups (0 .. 4)
+//     and chosen once per tile, so a k-step has no branch: its six fragment
+//     reads issue back to back, with no wait between them, and a scheduling
+//     barrier keeps them ahead of the MFMAs they overlap;
 //   * persistent workgroups walk a tile list laid out per expert as
 //     [n-tile][m-tile], so workgroups that run together share one weight
 //     tile; tile ids are split into one contiguous range per XCD (workgroup b
@@ -176,6 +180,8 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E_loc
     __syncthreads();
 }
 
+template <int N> struct IntC { static constexpr int value = N; };
+
 template <int WN, int MODE, bool F16, int OUT, int NB>
 __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
     typedef typename OutType<OUT>::type OutT;
@@ -271,16 +277,6 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
                 dma16(b_src[j & 1] + static_cast<int64_t>(kt * KS + (j >> 1)) * 2 * kFragElems, &s_b[st][bq][j][0]);
             }
         };
-        auto read_frags = [&](u32x4 (&fa)[TM], u32x4 (&fb)[2], int st, int ks) {
-            const int kg = ks * 2 + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                if (i < na)
-                    fa[i] = *reinterpret_cast<const u32x4*>(&s_a[st][lds_off(mh * BM + i * 32 + (lane & 31), kg)]);
-            fb[0] = *reinterpret_cast<const u32x4*>(&s_b[st][nq][2 * ks][lane * 8]);
-            fb[1] = *reinterpret_cast<const u32x4*>(&s_b[st][nq][2 * ks + 1][lane * 8]);
-        };
-
         floatx16 acc[TM][2];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -294,50 +290,75 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int q = 0; q + 1 < NB; ++q) issue(min(q, nk - 1), q);
 
-        u32x4 fa_cur[TM], fb_cur[2], fa_nxt[TM], fb_nxt[2];
-        static_assert(KS == 2, "the stage schedule below is written for two k-steps");
-        // 32-row groups past the segment are skipped (wave-uniform branch)
-        auto mfmas = [&](const u32x4 (&fa)[TM], const u32x4 (&fb)[2]) {
+        // The k-loop for NA active 32-row groups (0: an idle half that only copies
+        // and synchronises).  NA is fixed per tile, so a k-step is one basic block:
+        // its fragment reads and MFMAs interleave with no wait between reads.
+        auto kloop = [&](auto nac) {
+            constexpr int NA = decltype(nac)::value;
+            u32x4 fa_cur[TM], fb_cur[2], fa_nxt[TM], fb_nxt[2];
+            auto read_frags = [&](u32x4 (&fa)[TM], u32x4 (&fb)[2], int st, int ks) {
+                const int kg = ks * 2 + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (i < na) {
+                for (int i = 0; i < NA; ++i)
+                    fa[i] = *reinterpret_cast<const u32x4*>(&s_a[st][lds_off(mh * BM + i * 32 + (lane & 31), kg)]);
+                fb[0] = *reinterpret_cast<const u32x4*>(&s_b[st][nq][2 * ks][lane * 8]);
+                fb[1] = *reinterpret_cast<const u32x4*>(&s_b[st][nq][2 * ks + 1][lane * 8]);
+            };
+            auto mfmas = [&](const u32x4 (&fa)[TM], const u32x4 (&fb)[2]) {
+#pragma unroll
+                for (int i = 0; i < NA; ++i) {
                     acc[i][0] = mfma32<F16>(fa[i], fb[0], acc[i][0]);
                     acc[i][1] = mfma32<F16>(fa[i], fb[1], acc[i][1]);
                 }
-            }
-        };
-        // One k-tile from ring stage st, entered with its first k-step's fragments
-        // in fa_cur/fb_cur.  k-step 0: read k-step 1's fragments while the MFMAs
-        // run.  Then wait for this thread's copies of the next stage and meet the
-        // other waves (the next stage has landed everywhere, and nobody still reads
-        // the stage about to be refilled) while those MFMAs drain; refill that stage
-        // with k-tile kt+NB-1.  k-step 1: read the next stage's first fragments
-        // while its MFMAs run.  An idle half only copies and synchronises.
-        auto step = [&](int kt, int st) {
-            if (active) {
-                read_frags(fa_nxt, fb_nxt, st, 1);
-                mfmas(fa_cur, fb_cur);
-            }
-            wait_vmcnt<LOADS * (NB - 3)>();
+            };
+            static_assert(KS == 2, "the stage schedule below is written for two k-steps");
+            // One k-tile from ring stage st, entered with its first k-step's fragments
+            // in fa_cur/fb_cur.  k-step 0: read k-step 1's fragments while the MFMAs
+            // run.  Then wait for this thread's copies of the next stage and meet the
+            // other waves (the next stage has landed everywhere, and nobody still reads
+            // the stage about to be refilled) while those MFMAs drain; refill that stage
+            // with k-tile kt+NB-1.  k-step 1: read the next stage's first fragments
+            // while its MFMAs run.  A scheduling barrier after each batch of reads
+            // keeps them ahead of the MFMAs (left alone, the compiler sinks each
+            // read next to its use and waits for it there).
+            auto step = [&](int kt, int st) {
+                if constexpr (NA > 0) {
+                    read_frags(fa_nxt, fb_nxt, st, 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    asm volatile("" ::: "memory");
+                    mfmas(fa_cur, fb_cur);
+                }
+                wait_vmcnt<LOADS * (NB - 3)>();
+                __builtin_amdgcn_s_barrier();
+                issue(min(kt + NB - 1, nk - 1), (st + NB - 1) % NB);
+                if constexpr (NA > 0) {
+                    read_frags(fa_cur, fb_cur, (st + 1) % NB, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    asm volatile("" ::: "memory");
+                    mfmas(fa_nxt, fb_nxt);
+                }
+            };
+            // stage 0 must have landed before its first fragments are read
+            wait_vmcnt<LOADS * (NB - 2)>();
             __builtin_amdgcn_s_barrier();
-            issue(min(kt + NB - 1, nk - 1), (st + NB - 1) % NB);
-            if (active) {
-                read_frags(fa_cur, fb_cur, (st + 1) % NB, 0);
-                mfmas(fa_nxt, fb_nxt);
+            if constexpr (NA > 0) read_frags(fa_cur, fb_cur, 0, 0);
+            int kt0 = 0;
+            for (; kt0 + NB <= nk; kt0 += NB) {
+#pragma unroll
+                for (int q = 0; q < NB; ++q) step(kt0 + q, q);
             }
+#pragma unroll
+            for (int q = 0; q + 1 < NB; ++q)
+                if (kt0 + q < nk) step(kt0 + q, q);
         };
-        // stage 0 must have landed before its first fragments are read
-        wait_vmcnt<LOADS * (NB - 2)>();
-        __builtin_amdgcn_s_barrier();
-        if (active) read_frags(fa_cur, fb_cur, 0, 0);
-        int kt0 = 0;
-        for (; kt0 + NB <= nk; kt0 += NB) {
-#pragma unroll
-            for (int q = 0; q < NB; ++q) step(kt0 + q, q);
+        static_assert(TM == 4, "the dispatch below covers 0 .. 4 active row groups");
+        switch (active ? na : 0) {
+            case 4: kloop(IntC<4>{}); break;
+            case 3: kloop(IntC<3>{}); break;
+            case 2: kloop(IntC<2>{}); break;
+            case 1: kloop(IntC<1>{}); break;
+            default: kloop(IntC<0>{}); break;
         }
-#pragma unroll
-        for (int q = 0; q + 1 < NB; ++q)
-            if (kt0 + q < nk) step(kt0 + q, q);
 
         // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 tile
         if (active) {
@@ -379,8 +400,6 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 // tiles are added in wave order through LDS by all threads, which then apply
 // the epilogue.
 // ---------------------------------------------------------------------------
-template <int N> struct IntC { static constexpr int value = N; };
-
 // Raw buffer resource over the activation matrix (stride 0, byte-addressed):
 // offsets at or past kBufferRange load zeros.  The launcher keeps every valid
 // offset below kBufferRange.
