@@ -318,9 +318,11 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
             // other waves (the next stage has landed everywhere, and nobody still reads
             // the stage about to be refilled) while those MFMAs drain; refill that stage
             // with k-tile kt+NB-1.  k-step 1: read the next stage's first fragments
-            // while its MFMAs run.  A scheduling barrier after each batch of reads
-            // keeps them ahead of the MFMAs (left alone, the compiler sinks each
-            // read next to its use and waits for it there).
+            // while its MFMAs run.  After each batch of reads, a scheduling barrier
+            // and an empty asm statement with a memory clobber keep the reads ahead
+            // of the MFMAs (left alone, the compiler sinks each read next to its use
+            // and waits for it there); with both, the compiler places the rest in
+            // the order that measured fastest.
             auto step = [&](int kt, int st) {
                 if constexpr (NA > 0) {
                     read_frags(fa_nxt, fb_nxt, st, 1);
