@@ -226,6 +226,10 @@ def _gemm_case(B, counts, H, I, seed=7):
 @pytest.mark.parametrize("wdt", ["bf16", "f32"])
 @pytest.mark.parametrize("counts,H,I", [([37, 0, 300, 129], 256, 128), ([1], 64, 64), ([128, 128], 128, 192),
                                         ([0, 0, 5], 192, 64),
+                                        # the tiled kernel's k-loop is chosen per tile by the count of active
+                                        # 32-row groups in each 128-row half: 96 and 70 rows give 3, the
+                                        # 200-row tile 4 and 3, 33 rows 2, and idle halves 0
+                                        ([96, 200, 70, 33], 256, 128),
                                         # few rows per expert on average: the weight-streaming kernel, with
                                         # experts of 0, 1, 31, 33, 64, 65 and 150 rows (row groups of 64)
                                         ([150, 0, 1, 31, 33, 0, 0, 64, 65, 0, 0, 0, 0, 0, 0, 0] + [0] * 16,
