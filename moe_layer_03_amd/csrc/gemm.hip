@@ -17,15 +17,16 @@
 //   * activation rows can be gathered straight from the unpacked input
 //     through the dispatch's row-to-token map (no packed copy);
 //   * both operands reach LDS through direct global->LDS copies (no register
-//     staging) into a ring of NB stages, so NB-1 k-tiles are always in flight;
-//     the kernel waits on its own copy counter (s_waitcnt vmcnt) and a raw
-//     barrier, since copies retire in order;
+//     staging) into a ring of NB = 4 stages: while one stage is read, the next
+//     has landed and the two after it are in flight; the kernel waits on its
+//     own copy counter (s_waitcnt vmcnt) and a raw barrier, since copies
+//     retire in order;
 //   * activations (A): 16-byte granules of 64-byte stage rows, XOR-swizzled by
 //     row group so fragment reads are bank-conflict free (16 lanes of a 128-bit
 //     read per pass over 64 banks); all NW waves read all 128 rows;
-//   * a stage is 32 k (24 KiB at NW = 4) and the ring is 6 deep, so about 5
-//     stages (~120 KiB per CU) are in flight: load throughput per CU is bound by
-//     bytes in flight, and this keeps it above what the MFMAs consume;
+//   * a stage is 32 k: 16 KiB of activations (256 rows x 64 bytes) and 16 KiB
+//     of weights (256 columns), 128 KiB for the ring; at the prefill shapes
+//     this copy path, not the MFMAs, sets the kernel's pace;
 //   * weights (B) are packed once in MFMA fragment order (one 1 KiB block per
 //     32 columns x 16 k, lane-major), the two 32-column halves of each
 //     64-column block side by side per 16 k: every copy and every fragment
