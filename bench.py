@@ -1,17 +1,28 @@
 #!/usr/bin/env python3
 """Throughput of one expert-parallel rank's share of the MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--only] [--graph]
 
 A step is one pass of the whole share -- route, dispatch (count, scan,
 scatter, pack), grouped gate/up GEMM with the SwiGLU epilogue, grouped down
 GEMM, combine -- over one batch of seeded synthetic inputs that are already
-resident in HBM.  The headline value times K steps of the fused entry point
-``moe_layer``; ``--graph`` captures that step in a HIP graph and replays it.
-A second timed region runs the same K steps through the staged entry points
-in the order ``moe_layer`` uses, with HIP events on the launch stream around
-every stage, so each kernel's average duration (and the dominant kernel's
-roofline) is measured live.  Prints one JSON line.
+resident in HBM.
+
+The headline value times K steps of the fused entry point ``moe_layer`` on
+the headline workload (default: the 6000-token prefill shard), with a HIP
+event before every step, so the line carries the wall-clock mean and the
+median and minimum step.  ``--graph`` captures that step in a HIP graph and
+replays it.  A second timed region runs the same K steps through the staged
+entry points in the order ``moe_layer`` uses, with HIP events on the launch
+stream around every stage, so each kernel's average duration (and the
+dominant kernel's roofline) is measured live.
+
+Unless ``--only`` is given, the other full-size workloads (decode shard,
+skewed prefill, whole layer) are measured the same way afterwards and
+reported under ``configs`` (the decode shard also under ``decode``).  The
+line also carries the MFMA and copy rates measured on this chip next to the
+published peaks, and the oracle timed on the host cores (headline workload).
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -25,10 +36,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16/fp16 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (prefill) / % HBM GB/s (decode), 1 GPU"
+OTHERS = ["decode_ep16_shard", "skewed_prefill", "whole_layer"]
+PRECISION = {
+    "router": "fp32 fma chain (canonical order) on bf16 x and router weight",
+    "gate_up": "bf16 x bf16 MFMA, fp32 accumulation",
+    "h": "fp16 (SwiGLU activations)",
+    "down": "fp16 x fp16 MFMA, fp32 accumulation (down weights bf16 -> fp16 at pack time)",
+    "y": "fp16 (expert outputs)",
+    "combine_out": "fp32",
+}
 
 
 def parse():
@@ -40,8 +60,10 @@ def parse():
     # 4-7 % slower than with 30
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="prefill_ep4_shard", choices=WORKLOAD_ORDER)
+    ap.add_argument("--only", action="store_true", help="measure the headline workload only")
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA and copy rate probes")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the timed region, run a plain device copy (torch.neg) of this many MiB twice, "
@@ -49,24 +71,58 @@ def parse():
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "The expert-parallel share shards by giving each rank its own expert range; run one process per "
-              "GPU with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def host_cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
+
+def measure_peaks(torch, B, dev):
+    """Dense bf16 MFMA rate (the library's probe kernel) and plain copy rate (torch), measured here."""
+    res = {}
+    blocks, iters = 2048, 4000
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    B.moe_probe_mfma_bf16(blocks, iters, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = 0
+    for _ in range(5):
+        flops += B.moe_probe_mfma_bf16(blocks, iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    res["mfma_bf16_tflops"] = round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    del sink
+    n = (1 << 30) // 4
+    src = torch.randn(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    res["copy_gbs"] = round(5 * 2 * n * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    res["copy_note"] = "1 GiB fp32 device copy (read + write bytes)"
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure(wl, steps, warmup, graph, copy_probe_mib=0):
+    """Time `steps` fused steps and `steps` staged steps of workload wl; returns (result dict, inputs)."""
     import numpy as np
     import torch
 
     from moe_layer_03_amd import binding as B
     from moe_layer_03_amd import workloads as W
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = W.WORKLOADS[args.workload]
     s = B.Shape.of(wl)
 
     t_gen = time.perf_counter()
@@ -85,7 +141,7 @@ def main():
     del g, u, d
     t_gen = time.perf_counter() - t_gen
 
-    i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+    i32, f32 = torch.int32, torch.float32
     cap = s.cap
     buf = dict(
         topk_idx=torch.empty((s.T, s.K), dtype=i32, device=dev),
@@ -100,6 +156,7 @@ def main():
         y=torch.empty((cap, s.H), dtype=torch.float16, device=dev),
         out=torch.empty((s.T, s.H), dtype=f32, device=dev),
         ws=torch.empty(max(B.moe_dispatch_workspace_bytes(s), 16), dtype=torch.uint8, device=dev),
+        ws_route=torch.empty(max(B.moe_route_workspace_bytes(s), 16), dtype=torch.uint8, device=dev),
     )
     stages = ["route", "dispatch", "gemm_gate_up", "gemm_down", "combine"]
     gather = wl.dtype == "bf16"
@@ -108,7 +165,7 @@ def main():
         b = buf
         if ev is not None:
             ev[0].record()
-        B.moe_route(s, x, w_router, bias, topk_idx=b["topk_idx"], topk_w=b["topk_w"])
+        B.moe_route(s, x, w_router, bias, topk_idx=b["topk_idx"], topk_w=b["topk_w"], ws=b["ws_route"])
         if ev is not None:
             ev[1].record()
         if gather:   # bf16: the gate/up GEMM reads token rows straight from x, as moe_layer does
@@ -134,8 +191,8 @@ def main():
         if ev is not None:
             ev[5].record()
 
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib * (1 << 20) // 4
+    if copy_probe_mib > 0:
+        n = copy_probe_mib * (1 << 20) // 4
         src = torch.randn(n, dtype=f32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(2):
@@ -150,51 +207,51 @@ def main():
     def fused_step():
         B.moe_layer(s, x, w_router, packed, bias, out=out_fused, ws=ws_layer)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         fused_step()
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps of the fused entry point (the headline value)
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
+    # timed region: K steps of the fused entry point, an event before each step and after the last
+    ev_f = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    if graph:
+        cgraph = torch.cuda.CUDAGraph()
         cap_stream = torch.cuda.Stream()
         cap_stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap_stream):
-            with torch.cuda.graph(graph, stream=cap_stream):
+            with torch.cuda.graph(cgraph, stream=cap_stream):
                 fused_step()
         torch.cuda.current_stream().wait_stream(cap_stream)
-        graph.replay()
+        cgraph.replay()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        run = cgraph.replay
     else:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            fused_step()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        run = fused_step
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev_f[k].record()
+        run()
+    ev_f[steps].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per_step = np.array([ev_f[k].elapsed_time(ev_f[k + 1]) for k in range(steps)])
 
     # second timed region: the same K steps through the staged entry points, with HIP events around every
     # stage on the launch stream (per-stage durations and the dominant kernel's roofline)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         step(events[k])
     torch.cuda.synchronize()
-    ms_staged = (time.perf_counter() - t0) * 1e3 / args.steps
-    stage_ms = {name: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
+    ms_staged = (time.perf_counter() - t0) * 1e3 / steps
+    stage_ms = {name: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(steps)]))
                 for i, name in enumerate(stages)}
 
     counts = buf["counts"].cpu().numpy()
     n_loc = int(buf["offsets"][-1].item())
-
-    # the staged step and the fused entry point launch the same kernels: same bits
+    # the staged step and the fused entry point compute the same bits
     fused_equal = bool(torch.equal(buf["out"], out_fused))
 
     # algorithmic work (route + expert FFN) and bytes (active local experts' weights, router weight,
@@ -209,59 +266,131 @@ def main():
     # dominant kernel: the gate/up grouped GEMM (two thirds of the FLOPs and of the weight bytes)
     gu_flops = n_loc * 2 * H * 2 * I
     gu_bytes = active * 2 * H * I * 2 + n_loc * H * 2 + n_loc * I * 2
-    roofline = None
-    # the library's choice: the weight-streaming kernel when an evenly routed expert gets <= 64 rows
-    skinny = T * wl.K <= 64 * E
+    skinny = T * wl.K <= 64 * E   # the library's choice: weight streaming when an even expert gets <= 64 rows
     kname = ("grouped_gemm_skinny_kernel<SwiGLU,bf16,fp16,4> (gate/up)" if skinny
              else "grouped_gemm_kernel<4,SwiGLU,bf16,fp16,4> (gate/up)")
-    if stage_ms is not None:
-        t_gu = stage_ms["gemm_gate_up"] * 1e-3
-        if gu_flops / max(gu_bytes, 1) >= RIDGE:
-            ach = gu_flops / t_gu / 1e12
-            roofline = dict(kernel=kname, bound="mfma",
-                            achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                            frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(wl.name),
-                            per_launch=dict(flops=gu_flops, us=round(t_gu * 1e6, 2)))
-        else:
-            ach = gu_bytes / t_gu / 1e9
-            roofline = dict(kernel=kname, bound="hbm",
-                            achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                            frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(wl.name),
-                            per_launch=dict(bytes=gu_bytes, us=round(t_gu * 1e6, 2)))
+    t_gu = stage_ms["gemm_gate_up"] * 1e-3
+    if gu_flops / max(gu_bytes, 1) >= RIDGE:
+        ach = gu_flops / t_gu / 1e12
+        roofline = dict(kernel=kname, bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                        frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=measured_traffic(wl.name),
+                        per_launch=dict(flops=gu_flops, us=round(t_gu * 1e6, 2)))
+    else:
+        ach = gu_bytes / t_gu / 1e9
+        roofline = dict(kernel=kname, bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(ach / PEAK_HBM_GBS, 4), traffic=measured_traffic(wl.name),
+                        per_launch=dict(bytes=gu_bytes, us=round(t_gu * 1e6, 2)))
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, args.cpu_tokens)
-
-    line = {
-        "metric": METRIC,
-        "value": round(T / sec, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    res = {
+        "workload": wl.name,
+        "config": {"T": T, "H": H, "E": E, "K": wl.K, "I": I, "local_experts": [wl.e_begin, wl.e_end],
+                   "zipf_s": wl.zipf_s, "seed": wl.seed, "mode": "graph" if graph else "eager"},
+        "steps": steps,
         "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32-in/bf16-mfma",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no trained weights)",
-        "config": {"workload": wl.name, "T": T, "H": H, "E": E, "K": wl.K, "I": I,
-                   "local_experts": [wl.e_begin, wl.e_end], "zipf_s": wl.zipf_s, "seed": wl.seed,
-                   "mode": "graph" if args.graph else "eager"},
+        "ms_median": round(float(np.median(per_step)), 4),
+        "ms_min": round(float(per_step.min()), 4),
+        "tokens_s": round(T / sec, 1),
         "tflops": round(flops / sec / 1e12, 2),
         "mfma_frac": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
         "gbs": round(bytes_alg / sec / 1e9, 1),
         "hbm_frac": round(bytes_alg / sec / 1e9 / PEAK_HBM_GBS, 4),
+        "alg_flops": flops,
+        "alg_bytes": bytes_alg,
         "n_loc": n_loc,
-        "expert_rows": {"min": int(counts.min()), "mean": round(float(counts.mean()), 2), "max": int(counts.max())},
+        "expert_rows": {"min": int(counts.min()), "mean": round(float(counts.mean()), 2), "max": int(counts.max()),
+                        "cv": round(float(counts.std() / counts.mean()), 4) if counts.mean() > 0 else None,
+                        "active": active},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "ms_per_step_staged": round(ms_staged, 4),
         "roofline": roofline,
-        "cpu_baseline": cpu,
         "fused_entry_bitwise_equal": fused_equal,
         "input_setup_s": round(t_gen, 1),
     }
+    del buf, ws_layer, out_fused, packed, x, w_router, bias
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "The expert-parallel share shards by giving each rank its own expert range; run one process per "
+              "GPU with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from moe_layer_03_amd import binding as B
+    from moe_layer_03_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.load()
+
+    wl = W.WORKLOADS[args.workload]
+    head, inp = measure(wl, args.steps, args.warmup, args.graph, args.copy_probe_mib)
+    print(f"[bench] {wl.name}: {head['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp, args.cpu_tokens)
+    del inp
+
+    configs = {wl.name: head}
+    if not args.only:
+        for name in OTHERS:
+            if name == wl.name:
+                continue
+            r, _ = measure(W.WORKLOADS[name], args.steps, args.warmup, args.graph)
+            configs[name] = r
+            print(f"[bench] {name}: {r['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+
+    peaks = None if args.no_peaks else measure_peaks(torch, B, dev)
+    if peaks is not None:
+        for r in configs.values():
+            r["mfma_frac_measured_peak"] = round(r["tflops"] / peaks["mfma_bf16_tflops"], 4)
+            r["hbm_frac_measured_copy"] = round(r["gbs"] / peaks["copy_gbs"], 4)
+
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "ms_median": head["ms_median"],
+        "ms_min": head["ms_min"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16/fp16" if wl.dtype == "bf16" else "f32-in/fp16-mfma",
+        "precision": PRECISION if wl.dtype == "bf16" else {"all_gemms": "fp16 x fp16 MFMA, fp32 accumulation"},
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; no trained weights)",
+        "config": dict(workload=wl.name, **head["config"]),
+        "tflops": head["tflops"],
+        "mfma_frac": head["mfma_frac"],
+        "gbs": head["gbs"],
+        "hbm_frac": head["hbm_frac"],
+        "n_loc": head["n_loc"],
+        "expert_rows": head["expert_rows"],
+        "stage_ms": head["stage_ms"],
+        "ms_per_step_staged": head["ms_per_step_staged"],
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "fused_entry_bitwise_equal": head["fused_entry_bitwise_equal"],
+        "decode": configs.get("decode_ep16_shard"),
+        "configs": {k: v for k, v in configs.items() if k != wl.name},
+        "peaks": {"spec_bf16_tflops": PEAK_BF16_TFLOPS, "spec_hbm_gbs": PEAK_HBM_GBS,
+                  **(peaks or {})},
+        "host_cpu": host_cpu_model(),
+        "input_setup_s": head["input_setup_s"],
+    }
+    if line["decode"] is not None and "decode_ep16_shard" in line["configs"]:
+        del line["configs"]["decode_ep16_shard"]
     print(json.dumps(line), flush=True)
 
 
@@ -291,8 +420,6 @@ def measured_traffic(workload):
 
 def cpu_baseline(wl, inp, n_tokens):
     """The oracle, as it is, on the first n_tokens tokens of the same workload (host cores)."""
-    import numpy as np
-
     import oracle
     from moe_layer_03_amd import workloads as W
 
@@ -320,7 +447,7 @@ def cpu_baseline(wl, inp, n_tokens):
     dt = time.perf_counter() - t0
     return {"value": round(n_tokens / dt, 1), "unit": "tokens/s", "cores": int(max(oracle.num_threads(), blas)),
             "kind": "oracle", "sample": f"first {n_tokens} of {wl.T} tokens, full route/dispatch/FFN/combine",
-            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count(), "host_cpu": host_cpu_model()}
 
 
 if __name__ == "__main__":

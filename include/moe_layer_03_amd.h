@@ -84,6 +84,34 @@ size_t moe_dispatch_workspace_bytes(const moe_shape* s);
  */
 size_t moe_route_workspace_bytes(const moe_shape* s);
 
+/*
+ * Where the screened path of moe_route() leaves its estimates in the
+ * workspace (host-only, no HIP call).  For callers that check the error bound
+ * on which the screening's exactness rests.
+ *
+ * After moe_route() ran with ws != NULL on a shape that takes the screened
+ * path, and its stream has synchronised, ws holds at these byte offsets
+ * (S = slices; slice s covers h in [s*H/S, (s+1)*H/S)):
+ *   part_offset: float32 [S][T][E], the bf16-MFMA estimate of slice s of
+ *                sum_h x[t,h] * w_router[h,e] (any summation order);
+ *   nx_offset:   float32 [S][T], sum over slice s of x[t,h]^2;
+ *   nw_offset:   float32 [S][E], sum over slice s of w_router[h,e]^2.
+ * With u = 2^-24 and Hu = H*u, the router then forms, in float32 and in this
+ * order:
+ *   A[t,e] = ((part[0] + part[1]) + ...) + part[S-1], plus bias[e] if given;
+ *   nX = sum_s nx[s][t], nW = sum_s nw[s][e] (ascending s);
+ *   D[t,e] = 5 Hu (sqrt(nX) (1 + 3 Hu) sqrt(nW)) + 2^-21 |A| + 1e-30;
+ * and its selection is exact because |A[t,e] - L[t,e]| <= D[t,e] for the
+ * canonical logit L of moe_route().  Returns MOE_ERR_UNSUPPORTED when
+ * (s, x_dtype, w_dtype) does not take the screened path.
+ */
+typedef struct moe_route_screen_info {
+    int32_t slices;
+    size_t part_offset, nx_offset, nw_offset;
+    size_t bytes;        /* == moe_route_workspace_bytes(s) */
+} moe_route_screen_info;
+int moe_route_screen_layout(const moe_shape* s, int x_dtype, int w_dtype, moe_route_screen_info* info);
+
 /* Bytes of scratch memory moe_layer() needs (host-only, no HIP call). */
 size_t moe_layer_workspace_bytes(const moe_shape* s);
 
@@ -145,7 +173,9 @@ int moe_route_from_logits(const moe_shape* s, const float* logits, int32_t* topk
  * every rank, so dispatch only selects the tokens routed to the rank's
  * experts, aggregates the routing information and prepares the GEMM input
  * buffers).
- *   topk_idx [T, K] int32 (from moe_route).
+ *   topk_idx [T, K] int32 (from moe_route).  Precondition: a token lists an
+ *       expert at most once (moe_route guarantees it); a row that repeats a
+ *       local expert gives undefined counts and row maps.
  *   counts (output) [E_loc] int32: pairs routed to expert e_begin + i.
  *   offsets (output) [E_loc + 1] int32: exclusive prefix sum of counts.
  *   row_token, row_slot (output) [cap] int32: token and slot of packed row r;
@@ -224,6 +254,18 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
               int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
               int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Measurement helpers (not part of the layer).  moe_probe_mfma_bf16 launches
+ * `blocks` workgroups of 8 waves, each wave issuing `iters` rounds of eight
+ * independent v_mfma_f32_32x32x16_bf16 with no memory traffic, and writes one
+ * float per thread to sink [blocks * 512] (device memory, caller-owned);
+ * moe_probe_mfma_bf16_flops gives the FLOPs of one such launch.  Timing the
+ * launch gives the dense bf16 MFMA rate the chip reaches under the current
+ * clocks, to set beside the published peak.
+ */
+int64_t moe_probe_mfma_bf16_flops(int blocks, int iters);
+int moe_probe_mfma_bf16(int blocks, int iters, float* sink, void* stream);
 
 /* Text of a status code (static storage). */
 const char* moe_status_string(int status);

@@ -36,10 +36,12 @@ MOE_EPI_NONE = 0
 MOE_EPI_SWIGLU = 1
 
 EXPORTED = [
-    "moe_dispatch_workspace_bytes", "moe_route_workspace_bytes", "moe_layer_workspace_bytes",
+    "moe_dispatch_workspace_bytes", "moe_route_workspace_bytes", "moe_route_screen_layout",
+    "moe_layer_workspace_bytes",
     "moe_packed_weight_bytes",
     "moe_pack_weights", "moe_route", "moe_route_from_logits", "moe_dispatch", "moe_grouped_gemm",
     "moe_combine", "moe_layer", "moe_status_string", "moe_last_hip_error",
+    "moe_probe_mfma_bf16_flops", "moe_probe_mfma_bf16",
 ]
 
 
@@ -52,6 +54,11 @@ class MoeError(RuntimeError):
 
 class _CShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "E", "K", "I", "e_begin", "e_end")]
+
+
+class _CScreenInfo(ctypes.Structure):
+    _fields_ = [("slices", ctypes.c_int32), ("part_offset", ctypes.c_size_t), ("nx_offset", ctypes.c_size_t),
+                ("nw_offset", ctypes.c_size_t), ("bytes", ctypes.c_size_t)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -105,6 +112,7 @@ def load() -> ctypes.CDLL:
     sigs = {
         "moe_dispatch_workspace_bytes": (sz, [_S]),
         "moe_route_workspace_bytes": (sz, [_S]),
+        "moe_route_screen_layout": (i32, [_S, i32, i32, ctypes.POINTER(_CScreenInfo)]),
         "moe_layer_workspace_bytes": (sz, [_S]),
         "moe_packed_weight_bytes": (sz, [_S]),
         "moe_pack_weights": (i32, [_S, _P, _P, _P, i32, _P, _P]),
@@ -116,6 +124,8 @@ def load() -> ctypes.CDLL:
         "moe_layer": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_last_hip_error": (ctypes.c_int32, []),
+        "moe_probe_mfma_bf16_flops": (ctypes.c_int64, [i32, i32]),
+        "moe_probe_mfma_bf16": (i32, [i32, i32, _P, _P]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -188,6 +198,15 @@ def moe_dispatch_workspace_bytes(s: Shape) -> int:
 
 def moe_route_workspace_bytes(s: Shape) -> int:
     return int(load().moe_route_workspace_bytes(ctypes.byref(s.c())))
+
+
+def moe_route_screen_layout(s: Shape, x_dtype: int = MOE_BF16, w_dtype: int = MOE_BF16) -> dict:
+    """Offsets of the screened router's estimates in its workspace (see the C header)."""
+    info = _CScreenInfo()
+    st = load().moe_route_screen_layout(ctypes.byref(s.c()), x_dtype, w_dtype, ctypes.byref(info))
+    _check("moe_route_screen_layout", st)
+    return dict(slices=int(info.slices), part_offset=int(info.part_offset), nx_offset=int(info.nx_offset),
+                nw_offset=int(info.nw_offset), bytes=int(info.bytes))
 
 
 def moe_layer_workspace_bytes(s: Shape) -> int:
@@ -346,3 +365,12 @@ def moe_layer(s: Shape, x: torch.Tensor, w_router: torch.Tensor, packed: torch.T
                           _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check("moe_layer", st)
     return out
+
+
+def moe_probe_mfma_bf16(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> int:
+    """Launch the MFMA rate probe; returns the FLOPs of the launch (measurement helper)."""
+    if sink.numel() < blocks * 512:
+        raise ValueError("sink needs blocks * 512 floats")
+    st = load().moe_probe_mfma_bf16(blocks, iters, _ptr(sink, torch.float32, None, "sink"), _stream(stream))
+    _check("moe_probe_mfma_bf16", st)
+    return int(load().moe_probe_mfma_bf16_flops(blocks, iters))

@@ -109,6 +109,13 @@ size_t moe_route_workspace_bytes(const moe_shape* s) {
     return route_screen_bytes(*s, MOE_BF16, MOE_BF16);
 }
 
+int moe_route_screen_layout(const moe_shape* s, int x_dtype, int w_dtype, moe_route_screen_info* info) {
+    MOE_TRY(check_shape(s));
+    if (info == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype)) return MOE_ERR_UNSUPPORTED;
+    return route_screen_layout(*s, x_dtype, w_dtype, info) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
 size_t moe_layer_workspace_bytes(const moe_shape* s) {
     if (check_shape(s) != MOE_OK) return 0;
     return carve_layer(*s, nullptr).bytes;

@@ -109,6 +109,9 @@ void set_last_hip_error(hipError_t e);
 // Launchers (defined in the kernel translation units).  Arguments are
 // validated by the entry points before these are called.
 size_t route_screen_bytes(const moe_shape& s, int x_dtype, int w_dtype);
+// Where the screened path leaves its estimates in the workspace; false when
+// the shape and dtypes do not take that path.
+bool route_screen_layout(const moe_shape& s, int x_dtype, int w_dtype, moe_route_screen_info* info);
 int launch_route(const moe_shape& s, const void* x, int x_dtype, const void* w, const float* bias,
                  int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes, hipStream_t st);
 int launch_route_from_logits(const moe_shape& s, const float* logits, int32_t* topk_idx, float* topk_w,

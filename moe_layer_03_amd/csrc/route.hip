@@ -788,6 +788,7 @@ struct ScreenWs {
     float* part;    // [S][T][E] estimate partial sums
     float* nx;      // [S][T] partial squared norms of token rows
     float* nw;      // [S][E] partial squared norms of router-weight columns
+    size_t off_part, off_nx, off_nw;   // byte offsets of part, nx, nw from the base
     size_t bytes;
 };
 
@@ -800,8 +801,11 @@ inline ScreenWs screen_layout(const moe_shape& s, void* base) {
     size_t off = 0;
     auto take = [&](size_t n) { char* q = p ? p + off : nullptr; off += align256(n); return q; };
     w.wT = reinterpret_cast<uint16_t*>(take(static_cast<size_t>(s.E) * s.H * 2));
+    w.off_part = off;
     w.part = reinterpret_cast<float*>(take(static_cast<size_t>(S) * s.T * s.E * 4));
+    w.off_nx = off;
     w.nx = reinterpret_cast<float*>(take(static_cast<size_t>(S) * s.T * 4));
+    w.off_nw = off;
     w.nw = reinterpret_cast<float*>(take(static_cast<size_t>(S) * s.E * 4));
     w.bytes = off;
     return w;
@@ -1426,6 +1430,17 @@ bool screen_eligible(const moe_shape& s, int x_dtype, int w_dtype) {
 
 size_t route_screen_bytes(const moe_shape& s, int x_dtype, int w_dtype) {
     return screen_eligible(s, x_dtype, w_dtype) ? screen_layout(s, nullptr).bytes : 0;
+}
+
+bool route_screen_layout(const moe_shape& s, int x_dtype, int w_dtype, moe_route_screen_info* info) {
+    if (!screen_eligible(s, x_dtype, w_dtype)) return false;
+    const ScreenWs w = screen_layout(s, nullptr);
+    info->slices = screen_slices(s.T, s.H);
+    info->part_offset = w.off_part;
+    info->nx_offset = w.off_nx;
+    info->nw_offset = w.off_nw;
+    info->bytes = w.bytes;
+    return true;
 }
 
 int launch_route(const moe_shape& s, const void* x, int x_dtype, const void* w, const float* bias,

@@ -142,3 +142,25 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_route_screen_layout_host_only():
+    """The screened router's workspace layout: regions in order, inside the workspace, and no layout for
+    shapes that do not take the screened path."""
+    s = B.Shape(T=6000, H=4096, E=128, K=8, I=1536, e_begin=0, e_end=32)
+    info = B.moe_route_screen_layout(s)
+    S, T, E = info["slices"], s.T, s.E
+    assert S >= 1 and s.H % S == 0
+    assert info["bytes"] == B.moe_route_workspace_bytes(s)
+    assert info["part_offset"] + S * T * E * 4 <= info["nx_offset"]
+    assert info["nx_offset"] + S * T * 4 <= info["nw_offset"]
+    assert info["nw_offset"] + S * E * 4 <= info["bytes"]
+    for bad in (B.Shape(T=511, H=4096, E=128, K=8, I=64, e_begin=0, e_end=128),
+                B.Shape(T=600, H=192, E=128, K=8, I=64, e_begin=0, e_end=128),
+                B.Shape(T=600, H=256, E=64, K=8, I=64, e_begin=0, e_end=64)):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_route_screen_layout(bad)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route_screen_layout(s, B.MOE_F32, B.MOE_F32)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED

@@ -157,6 +157,94 @@ def test_route_screened_bias_ties_and_degenerate(B):
     assert np.array_equal(idx, ri) and np.all(tw == 1.0)
 
 
+def _screen_bound(B, x, w, bias=None, K=8):
+    """Run the screened route with a workspace of our own, read back the MFMA
+    estimates and norms it leaves there, rebuild the interval [A - D, A + D]
+    the router uses (float32, in the documented order) and check that it holds
+    the canonical logit L of every (token, expert).  Returns max |A - L| / D."""
+    T, H = x.shape
+    E = w.shape[1]
+    s = B.Shape(T, H, E, K, 64, 0, E)
+    info = B.moe_route_screen_layout(s)
+    assert info["bytes"] == B.moe_route_workspace_bytes(s) > 0
+    ws = torch.empty(info["bytes"], dtype=torch.uint8, device="cuda")
+    bt = to_torch(bias) if bias is not None else None
+    idx, tw, _ = B.moe_route(s, to_torch(x), to_torch(w), bt, ws=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    S = info["slices"]
+
+    def view(off, *shape):
+        n = int(np.prod(shape))
+        return raw[off:off + 4 * n].view(np.float32).reshape(shape)
+
+    part = view(info["part_offset"], S, T, E)
+    nx = view(info["nx_offset"], S, T)
+    nw = view(info["nw_offset"], S, E)
+    A = part[0].copy()
+    for sl in range(1, S):
+        A = A + part[sl]
+    if bias is not None:
+        A = A + np.asarray(bias, np.float32)[None, :]
+    nX, nW = nx[0].copy(), nw[0].copy()
+    for sl in range(1, S):
+        nX, nW = nX + nx[sl], nW + nw[sl]
+    f = np.float32
+    Hu = f(H) * f(2.0 ** -24)
+    sx = np.sqrt(nX) * (f(1.0) + f(3.0) * Hu)
+    D = (f(5.0) * Hu) * (sx[:, None] * np.sqrt(nW)[None, :]) + f(2.0 ** -21) * np.abs(A) + f(1e-30)
+    assert A.dtype == np.float32 and D.dtype == np.float32
+    L = oracle.router_logits(W.as_f32(x), W.as_f32(w), bias)
+    gap = np.abs(A.astype(np.float64) - L.astype(np.float64))
+    worst = np.unravel_index(np.argmax(gap / D), gap.shape)
+    assert np.all(gap <= D.astype(np.float64)), f"estimate error beyond the bound at (t, e) = {worst}"
+    assert np.all((A - D) <= L) and np.all(L <= (A + D)), "the router's float32 interval misses a canonical logit"
+    ri, rw, _ = oracle.route(W.as_f32(x), W.as_f32(w), bias, K)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    assert np.abs(tw.cpu().numpy() - rw).max() <= 1e-6
+    return float((gap / D).max())
+
+
+def _bound_inputs(kind, T=1024, H=4096, seed=11):
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((H, 128), dtype=np.float32) * np.float32(0.02)
+    x = rng.standard_normal((T, H), dtype=np.float32)
+    if kind == "scaled64":
+        x *= np.float32(64.0)
+    elif kind == "cancelling":
+        # products cancel in pairs: x[2i+1] = -x[2i] and, for 90 % of the pairs, w[2i+1] = w[2i];
+        # the logits are small against sum |x w|, the quantity the bound scales with
+        x[:, 1::2] = -x[:, 0::2]
+        wb = W.as_f32(_bf16(w))
+        keep = rng.random(H // 2) < 0.9
+        wb[1::2][keep] = wb[0::2][keep]
+        w = wb
+    elif kind == "exponent_spread":
+        # elements spread over 2^-24 .. 2^24; a few rows at 2^40 (every product and square stays normal)
+        x *= np.exp2(rng.integers(-24, 25, size=(T, H))).astype(np.float32)
+        x[::97] *= np.float32(2.0 ** 40)
+    else:
+        raise ValueError(kind)
+    return _bf16(x), _bf16(w)
+
+
+@pytest.mark.parametrize("kind", ["scaled64", "cancelling", "exponent_spread"])
+def test_route_screened_error_bound(B, kind):
+    """The screened router's MFMA estimates stay within the bound D of the
+    canonical logits on every (token, expert), for inputs built to stress it."""
+    x, w = _bound_inputs(kind)
+    ratio = _screen_bound(B, x, w)
+    print(f"[{kind}] max |A - L| / D = {ratio:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["prefill_ep4_shard", "skewed_prefill"])
+def test_route_screened_error_bound_workloads(B, name):
+    """The same bound on the full prefill-shard inputs and on the skewed inputs (Zipf router bias)."""
+    wl = W.WORKLOADS[name]
+    ratio = _screen_bound(B, W.gen_x(wl), W.gen_router(wl), W.gen_bias(wl), wl.K)
+    print(f"[{name}] max |A - L| / D = {ratio:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("E,K", [(128, 8), (8, 2), (300, 16), (1024, 64)])
 def test_route_from_logits_ties(B, E, K):
     T = 257
@@ -247,6 +335,29 @@ def test_grouped_gemm_exact_integers(B, counts, H, I, wdt):
     off = to_torch(offsets)
     c1 = B.moe_grouped_gemm(s, at, off, packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_NONE, c_dtype=torch.float32)
     h = (np.random.default_rng(8).integers(-4, 5, size=(s.cap, I)) / 16).astype(np.float32)
+    c2 = B.moe_grouped_gemm(s, to_torch(h.astype(np.float16)), off, packed, B.MOE_GEMM_DOWN, B.MOE_EPI_NONE,
+                            c_dtype=torch.float32)
+    torch.cuda.synchronize()
+    c1, c2 = c1.cpu().numpy(), c2.cpu().numpy()
+    for e in range(len(counts)):
+        r0, r1 = offsets[e], offsets[e + 1]
+        gu = np.concatenate([a[r0:r1] @ wg[e], a[r0:r1] @ wu[e]], axis=1)
+        assert np.array_equal(c1[r0:r1], gu), f"gate/up expert {e}"
+        assert np.array_equal(c2[r0:r1], h[r0:r1] @ wd[e]), f"down expert {e}"
+
+
+def test_grouped_gemm_exact_integers_many_tiles(B):
+    """64 experts x 300 rows, 3072 gate/up columns: 1536 tiles, so every
+    persistent workgroup of the tiled kernel runs several tiles (ring and LDS
+    reused across tiles, the per-XCD tile ranges); bit-exact on integer-grid
+    operands for both problems."""
+    counts = [300] * 64
+    s, offsets, a, wg, wu, wd = _gemm_case(B, counts, 512, 1536, seed=12)
+    packed = B.moe_pack_weights(s, to_torch(_bf16(wg)), to_torch(_bf16(wu)), to_torch(_bf16(wd)))
+    off = to_torch(offsets)
+    c1 = B.moe_grouped_gemm(s, to_torch(_bf16(a)), off, packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_NONE,
+                            c_dtype=torch.float32)
+    h = (np.random.default_rng(13).integers(-4, 5, size=(s.cap, 1536)) / 16).astype(np.float32)
     c2 = B.moe_grouped_gemm(s, to_torch(h.astype(np.float16)), off, packed, B.MOE_GEMM_DOWN, B.MOE_EPI_NONE,
                             c_dtype=torch.float32)
     torch.cuda.synchronize()
