@@ -19,8 +19,9 @@
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers (HIP device memory), row-major,
  *     owned by the caller, 16-byte aligned.  The library never allocates
- *     or frees memory and keeps no global state besides a per-thread copy
- *     of the last HIP error code.
+ *     or frees memory.  Its global state is a per-thread copy of the last
+ *     HIP error code and, for moe_layer_noalloc, one static workspace array
+ *     per GPU with its device address cached per device.
  *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
  *     A call only enqueues work on it and returns; outputs are valid once
  *     the stream has synchronised, and inputs must stay alive until then.
@@ -254,6 +255,31 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
               int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
               int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_noalloc -- moe_layer() for callers that cannot allocate device
+ * memory: code under stream (graph) capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, outputs and bits as moe_layer()
+ * without ws / ws_bytes: the workspace is a static device array of
+ * MOE_LAYER_NOALLOC_MAX_WS_BYTES bytes inside the library, one per GPU, held
+ * by that GPU until the process ends.  The call allocates nothing (no
+ * hipMalloc, no library allocation).
+ *   Limit: moe_layer_workspace_bytes(s) <= MOE_LAYER_NOALLOC_MAX_WS_BYTES
+ *   (64 MiB: decode-sized batches, e.g. 128 tokens x top-8 over 8 local
+ *   experts of hidden 4096 needs about 20 MiB), else MOE_ERR_WORKSPACE and
+ *   nothing is enqueued.
+ *   The first call on each GPU (with that GPU current) resolves the array's
+ *   address with hipGetSymbolAddress; make it outside stream capture.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *   GPU (different streams, or threads, without ordering between them) race
+ *   and give undefined results.  No part of the array needs to start zeroed:
+ *   every call writes each workspace byte it reads.
+ */
+#define MOE_LAYER_NOALLOC_MAX_WS_BYTES ((size_t)64 << 20)
+int moe_layer_noalloc(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
+                      const float* bias, const void* packed, float* out,
+                      int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                      int32_t* row_token, int32_t* row_slot, int32_t* slot_row, void* stream);
 
 /*
  * Measurement helpers (not part of the layer).  moe_probe_mfma_bf16 launches

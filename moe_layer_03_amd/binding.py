@@ -41,8 +41,10 @@ EXPORTED = [
     "moe_packed_weight_bytes",
     "moe_pack_weights", "moe_route", "moe_route_from_logits", "moe_dispatch", "moe_grouped_gemm",
     "moe_combine", "moe_layer", "moe_status_string", "moe_last_hip_error",
-    "moe_probe_mfma_bf16_flops", "moe_probe_mfma_bf16",
+    "moe_probe_mfma_bf16_flops", "moe_probe_mfma_bf16", "moe_layer_noalloc",
 ]
+
+MOE_LAYER_NOALLOC_MAX_WS_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -124,6 +126,7 @@ def load() -> ctypes.CDLL:
         "moe_layer": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_last_hip_error": (ctypes.c_int32, []),
+        "moe_layer_noalloc": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_probe_mfma_bf16_flops": (ctypes.c_int64, [i32, i32]),
         "moe_probe_mfma_bf16": (i32, [i32, i32, _P, _P]),
     }
@@ -364,6 +367,28 @@ def moe_layer(s: Shape, x: torch.Tensor, w_router: torch.Tensor, packed: torch.T
                           _ptr(slot_row, torch.int32, s.T * s.K, "slot_row"),
                           _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check("moe_layer", st)
+    return out
+
+
+def moe_layer_noalloc(s: Shape, x: torch.Tensor, w_router: torch.Tensor, packed: torch.Tensor,
+                      bias: Optional[torch.Tensor] = None, out=None, *, topk_idx=None, topk_w=None, counts=None,
+                      offsets=None, row_token=None, row_slot=None, slot_row=None, stream=None) -> torch.Tensor:
+    """moe_layer with the library's static per-GPU workspace (the C call allocates nothing)."""
+    if out is None:
+        out = _empty((s.T, s.H), torch.float32, x.device)
+    cap = s.cap
+    st = load().moe_layer_noalloc(ctypes.byref(s.c()), _ptr(x, None, s.T * s.H, "x"), _dt(x),
+                                  _ptr(w_router, None, s.H * s.E, "w_router"), _dt(w_router),
+                                  _ptr(bias, torch.float32, s.E, "bias"), _ptr(packed, torch.uint8, None, "packed"),
+                                  _ptr(out, torch.float32, s.T * s.H, "out"),
+                                  _ptr(topk_idx, torch.int32, s.T * s.K, "topk_idx"),
+                                  _ptr(topk_w, torch.float32, s.T * s.K, "topk_w"),
+                                  _ptr(counts, torch.int32, s.E_loc, "counts"),
+                                  _ptr(offsets, torch.int32, s.E_loc + 1, "offsets"),
+                                  _ptr(row_token, torch.int32, cap, "row_token"),
+                                  _ptr(row_slot, torch.int32, cap, "row_slot"),
+                                  _ptr(slot_row, torch.int32, s.T * s.K, "slot_row"), _stream(stream))
+    _check("moe_layer_noalloc", st)
     return out
 
 

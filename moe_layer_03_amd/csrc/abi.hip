@@ -4,14 +4,48 @@
 #include <stdint.h>
 
 #include <cstddef>
+#include <mutex>
 
 #include "common.hpp"
 #include "route_prefetch.hpp"
+
+// Workspace of moe_layer_noalloc: one copy per GPU, held by that GPU from the
+// moment the library's code is loaded on it until the process ends.  In host
+// code this name is only a handle for hipGetSymbolAddress, never an address.
+__device__ __attribute__((aligned(256))) unsigned char scratch[MOE_LAYER_NOALLOC_MAX_WS_BYTES];
 
 namespace moe {
 
 namespace {
 thread_local int32_t g_last_hip_error = 0;
+
+// Device address of `scratch` on each GPU, resolved once per device (with that
+// device current) on the first moe_layer_noalloc call there.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int32_t>(e);
+        return MOE_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            g_last_hip_error = static_cast<int32_t>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return MOE_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -269,6 +303,18 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
     MOE_TRY(launch_grouped_gemm(*s, w.h, MOE_F16, nullptr, off, pk, MOE_GEMM_DOWN, MOE_EPI_NONE, w.y, MOE_F16, st));
     MOE_TRY(launch_combine(*s, w.y, MOE_F16, sr, tw, out, st));
     return MOE_OK;
+}
+
+int moe_layer_noalloc(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
+                      const float* bias, const void* packed, float* out, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
+                      void* stream) {
+    MOE_TRY(check_shape(s));
+    if (carve_layer(*s, nullptr).bytes > MOE_LAYER_NOALLOC_MAX_WS_BYTES) return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    MOE_TRY(scratch_of_current_device(&ws));
+    return moe_layer(s, x, x_dtype, w_router, w_dtype, bias, packed, out, topk_idx, topk_w, counts, offsets,
+                     row_token, row_slot, slot_row, ws, MOE_LAYER_NOALLOC_MAX_WS_BYTES, stream);
 }
 
 const char* moe_status_string(int status) {
