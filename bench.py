@@ -19,7 +19,10 @@ dominant kernel's roofline) is measured live.
 
 Unless ``--only`` is given, the other full-size workloads (decode shard,
 skewed prefill, whole layer) are measured the same way afterwards and
-reported under ``configs`` (the decode shard also under ``decode``).  The
+reported under ``configs`` (the decode shard under ``decode``), followed by
+the grouped-GEMM micro-benchmark of a decode rank: every local expert
+activated by one token, for 32, 16, 8, 4 and 2 local experts
+(``gemm_single_token_sweep``).  The
 line also carries the MFMA and copy rates measured on this chip next to the
 published peaks, and the oracle timed on the host cores (headline workload).
 Prints one JSON line.
@@ -312,6 +315,63 @@ def measure(wl, steps, warmup, graph, copy_probe_mib=0):
     return res, inp
 
 
+def gemm_single_token_sweep(e_locs=(32, 16, 8, 4, 2), reps=50, warmup=20):
+    """The grouped expert GEMMs (gate/up with SwiGLU, then down) with every local expert activated by exactly
+    one token, for several local-expert counts: the GEMM micro-benchmark of one expert-parallel decode rank.
+    Weights stream from HBM (the packed copy of each count is read once per repetition)."""
+    import numpy as np
+    import torch
+
+    from moe_layer_03_amd import binding as B
+    from moe_layer_03_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    base = W.WORKLOADS["decode_ep16_shard"]
+    g, u, d = W.gen_experts(base, range(max(e_locs)))
+    x = W.gen_x(base.replace(T=max(e_locs)))
+    out = []
+    for n in e_locs:
+        s = B.Shape(n, base.H, base.E, 1, base.I, 0, n)      # n tokens, one per local expert
+        gt, ut, dt_ = (torch.from_numpy(np.ascontiguousarray(a[:n])).view(torch.bfloat16).to(dev) for a in (g, u, d))
+        packed = B.moe_pack_weights(s, gt, ut, dt_)
+        del gt, ut, dt_
+        a = torch.from_numpy(np.ascontiguousarray(x[:n])).view(torch.bfloat16).to(dev)
+        offs = torch.arange(n + 1, dtype=torch.int32, device=dev)
+        h = torch.empty((n, base.I), dtype=torch.float16, device=dev)
+        y = torch.empty((n, base.H), dtype=torch.float16, device=dev)
+
+        def run(ev=None):
+            if ev is not None:
+                ev[0].record()
+            B.moe_grouped_gemm(s, a, offs, packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_SWIGLU, c=h)
+            if ev is not None:
+                ev[1].record()
+            B.moe_grouped_gemm(s, h, offs, packed, B.MOE_GEMM_DOWN, B.MOE_EPI_NONE, c=y)
+            if ev is not None:
+                ev[2].record()
+
+        for _ in range(warmup):
+            run()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for k in range(reps):
+            run(evs[k])
+        torch.cuda.synchronize()
+        gu = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+        dn = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+        tot = gu + dn
+        wbytes = n * 3 * base.H * base.I * 2
+        med = float(np.median(tot))
+        out.append({"local_experts": n, "us_gate_up": round(float(np.median(gu)), 2),
+                    "us_down": round(float(np.median(dn)), 2), "us_total": round(med, 2),
+                    "us_total_min": round(float(tot.min()), 2), "weight_bytes": wbytes,
+                    "gbs": round(wbytes / (med * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(wbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
+        del packed, a, h, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -347,6 +407,12 @@ def main():
             r, _ = measure(W.WORKLOADS[name], args.steps, args.warmup, args.graph)
             configs[name] = r
             print(f"[bench] {name}: {r['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+
+    sweep = None
+    if not args.only:
+        sweep = gemm_single_token_sweep()
+        print(f"[bench] single-token GEMM sweep: {[(r['local_experts'], r['us_total']) for r in sweep]}",
+              file=sys.stderr, flush=True)
 
     peaks = None if args.no_peaks else measure_peaks(torch, B, dev)
     if peaks is not None:
@@ -384,6 +450,7 @@ def main():
         "fused_entry_bitwise_equal": head["fused_entry_bitwise_equal"],
         "decode": configs.get("decode_ep16_shard"),
         "configs": {k: v for k, v in configs.items() if k != wl.name},
+        "gemm_single_token_sweep": sweep,
         "peaks": {"spec_bf16_tflops": PEAK_BF16_TFLOPS, "spec_hbm_gbs": PEAK_HBM_GBS,
                   **(peaks or {})},
         "host_cpu": host_cpu_model(),

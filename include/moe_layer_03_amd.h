@@ -202,8 +202,9 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int
  *   which = MOE_GEMM_DOWN: a [cap, I] fp16 (a_dtype MOE_F16); epilogue
  *       MOE_EPI_NONE -> c [cap, H].
  *   a_rows: NULL, then a holds the packed rows ([cap, Kd]); or [cap] int32,
- *       then packed row r is row a_rows[r] of a (for instance a = x [T, H]
- *       and a_rows = the row_token of moe_dispatch: no packed copy needed).
+ *       then packed row r is row a_rows[r] of a, 0 <= a_rows[r] < T (for
+ *       instance a = x [T, H] and a_rows = the row_token of moe_dispatch: no
+ *       packed copy needed).
  *   c_dtype MOE_F32, MOE_BF16 or MOE_F16 (16-bit outputs round to nearest
  *   even; fp16 saturates at 65504); products accumulate in float32.  Rows
  *   >= N_loc are not written.

@@ -321,7 +321,9 @@ def _gemm_case(B, counts, H, I, seed=7):
                                         # few rows per expert on average: the weight-streaming kernel, with
                                         # experts of 0, 1, 31, 33, 64, 65 and 150 rows (row groups of 64)
                                         ([150, 0, 1, 31, 33, 0, 0, 64, 65, 0, 0, 0, 0, 0, 0, 0] + [0] * 16,
-                                         256, 128)])
+                                         256, 128),
+                                        # every expert activated by one token (the decode GEMM micro-benchmark)
+                                        ([1] * 32, 256, 128), ([1, 1], 512, 192)])
 def test_grouped_gemm_exact_integers(B, counts, H, I, wdt):
     """Both problems on integer-grid operands, float32 output: bit-exact in any order.
     bf16 weights multiply in bf16, float32 weights in fp16; down always in fp16."""
