@@ -33,6 +33,8 @@ microscaled for the scaled matrix instructions):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Sequence
 
 import numpy as np
@@ -58,23 +60,29 @@ def e4m3_values() -> np.ndarray:
     return v
 
 
-_POS = e4m3_values()[:0x7F]          # codes 0 .. 0x7E: the non-negative finite values, ascending
-
-
 def e4m3_encode(a: np.ndarray) -> np.ndarray:
-    """Nearest E4M3 code of each value (ties to the even code), magnitudes above
+    """Nearest E4M3 code of each value, ties to the even code, magnitudes above
     448 saturating to 448; the sign bit follows the sign of the input (so a small
-    negative value that rounds to zero gives -0, code 0x80).  uint8."""
+    negative value that rounds to zero gives -0, code 0x80).  uint8.
+
+    Written from the format: a magnitude 2^E * (1 + k/8) with E >= -6 has code
+    (E + 7) * 8 + k, so k is (m / 2^E - 1) * 8 rounded half to even (np.rint),
+    carrying into the exponent when it reaches 8; below 2^-6 the values are
+    k * 2^-9, k = m * 2^9 rounded half to even.  An even code is an even k."""
     a = np.asarray(a, dtype=np.float64)
     mag = np.minimum(np.abs(a), E4M3_MAX)
-    hi = np.clip(np.searchsorted(_POS, mag, side="left"), 0, _POS.size - 1)   # _POS[hi] >= mag
-    lo = np.clip(hi - 1, 0, _POS.size - 1)
-    d_lo = mag - _POS[lo]
-    d_hi = _POS[hi] - mag
-    pick = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(hi % 2 == 0, hi, lo)))
-    pick = np.where(mag == _POS[hi], hi, pick)
+    _, e = np.frexp(mag)
+    E = e.astype(np.int64) - 1                              # floor(log2 mag) for mag > 0
+    normal = mag >= 2.0 ** -6
+    Es = np.where(normal, E, 0)
+    k = np.rint((mag / np.exp2(Es.astype(np.float64)) - 1.0) * 8.0).astype(np.int64)
+    Es = np.where(k == 8, Es + 1, Es)
+    k = np.where(k == 8, 0, k)
+    code_normal = ((Es + 7) << 3) | k
+    code_sub = np.rint(mag * 512.0).astype(np.int64)
+    code = np.where(normal, code_normal, code_sub)
     sign = np.signbit(a).astype(np.int64)
-    return ((sign << 7) | pick).astype(np.uint8)
+    return ((sign << 7) | code).astype(np.uint8)
 
 
 def shared_exponent(block_amax: np.ndarray) -> np.ndarray:
@@ -136,9 +144,13 @@ def moe_layer(x, w_router, bias, K: int, e_begin: int, e_end: int,
     xq = fake_quant(np.asarray(x, dtype=np.float64), axis=1)
     n = int(d["offsets"][-1])
     y = np.zeros((n, H), dtype=np.float64)
-    for i in range(e_end - e_begin):
+
+    def one(i):                      # experts are independent: run them on a thread pool
         a, b = int(d["offsets"][i]), int(d["offsets"][i + 1])
         if b > a:
             y[a:b] = expert_ffn(xq[d["row_token"][a:b]], w_gate[i], w_up[i], w_down[i])
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(one, range(e_end - e_begin)))
     out = _moe.combine(y, d["slot_row"], w, T, H)
     return dict(topk_idx=idx, topk_w=w, logits=logits, y_packed=y, out=out, **d)

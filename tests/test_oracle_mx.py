@@ -35,7 +35,7 @@ def test_planted_emax_off_by_one(monkeypatch):
 
 
 def test_planted_ties_away_from_zero(monkeypatch):
-    pos = M.e4m3_values()[:0x7F]
+    pos = M.e4m3_values()[:0x7F]           # codes 0 .. 0x7E, ascending
 
     def bad(a):
         a = np.asarray(a, np.float64)
