@@ -47,10 +47,12 @@ extern "C" {
 #define MOE_ERR_WORKSPACE   (-3)   /* ws_bytes smaller than the matching *_workspace_bytes() */
 #define MOE_ERR_HIP         (-4)   /* a HIP launch failed; see moe_last_hip_error() */
 
-/* Element types.  MOE_F16 appears only for intermediates and GEMM outputs. */
-#define MOE_F32  0
-#define MOE_BF16 1
-#define MOE_F16  2
+/* Element types.  MOE_F16 appears only for intermediates and GEMM outputs;
+ * MOE_MXFP8 only for MXFP8 GEMM outputs (codes plus scales, see below). */
+#define MOE_F32   0
+#define MOE_BF16  1
+#define MOE_F16   2
+#define MOE_MXFP8 3
 
 /* Grouped-GEMM operand selector and epilogues. */
 #define MOE_GEMM_GATE_UP 0   /* A = packed tokens [*, H], B = gate and up weights of each expert  */
@@ -256,6 +258,78 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
               int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
               int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MXFP8 expert GEMMs ("Quantification": the deployment quantises the model
+ * with the MXFP8 microscaling scheme, converting the weights statically).
+ * The format is the Open Compute Project Microscaling MXFP8 with E4M3
+ * elements: 32 consecutive elements along the reduction dimension K share one
+ * E8M0 scale 2^(e - 127) (a byte e); an element is an FP8 E4M3 code (bias 7,
+ * largest finite 448, no infinities).  A block converts with shared exponent
+ * floor(log2(max |v|)) - 8, clamped to [-127, 127] (-127 for an all-zero
+ * block), and elements v / 2^shared rounded to the nearest E4M3 value, ties to
+ * the even code, saturating at +-448.  Both operands of every expert GEMM are
+ * MXFP8, multiplied on gfx950's scaled MFMA with float32 accumulation:
+ * weights quantised per output column along K (H for gate/up, I for down),
+ * token rows x per token along H, SwiGLU activations h per row along I.
+ * Activation data: codes [rows][K] (uint8), scales [rows][K/32] (uint8 E8M0).
+ * Every MXFP8 call needs H and I multiples of 256 (else MOE_ERR_UNSUPPORTED).
+ */
+
+/* Bytes of the MXFP8-packed weights of the E_loc local experts (host-only):
+ * 3*E_loc*H*I bytes of codes plus one scale byte per 32 of them. */
+size_t moe_packed_weight_bytes_mxfp8(const moe_shape* s);
+
+/*
+ * moe_pack_weights_mxfp8 -- static conversion of the local experts' weights
+ * (w_gate, w_up [E_loc, H, I], w_down [E_loc, I, H], MOE_BF16 or MOE_F32) to
+ * MXFP8, per output column along K, into the layout the MXFP8 grouped GEMM
+ * streams.  packed: moe_packed_weight_bytes_mxfp8(s) bytes, written; opaque.
+ */
+int moe_pack_weights_mxfp8(const moe_shape* s, const void* w_gate, const void* w_up, const void* w_down,
+                           int dtype, void* packed, void* stream);
+
+/*
+ * moe_quantize_mxfp8 -- MXFP8 conversion of rows along their last axis:
+ *   x [rows, K] (MOE_BF16 or MOE_F32), K a multiple of 32 ->
+ *   codes [rows, K] uint8 and scales [rows, K/32] uint8.  rows >= 0.
+ */
+int moe_quantize_mxfp8(int64_t rows, int32_t K, const void* x, int x_dtype, uint8_t* codes, uint8_t* scales,
+                       void* stream);
+
+/*
+ * moe_grouped_gemm_mxfp8 -- moe_grouped_gemm() on MXFP8 operands.
+ *   a, a_scales: activation codes and scales (rows of K = H for gate/up, I
+ *       for down); a_rows as in moe_grouped_gemm (NULL: a holds the packed
+ *       rows; else packed row r reads row a_rows[r] of a and of a_scales,
+ *       0 <= a_rows[r] < T).
+ *   packed: moe_pack_weights_mxfp8() output for the same shape.
+ *   which / epilogue as in moe_grouped_gemm.  c_dtype MOE_F32, MOE_BF16 or
+ *   MOE_F16 (rows of the plain product, or of h for MOE_EPI_SWIGLU), or, with
+ *   MOE_EPI_SWIGLU only, MOE_MXFP8: c receives the codes of h [cap, I] and
+ *   c_scales its scales [cap, I/32] (c_scales is ignored otherwise).
+ *   Rows >= N_loc are not written.
+ */
+int moe_grouped_gemm_mxfp8(const moe_shape* s, const uint8_t* a, const uint8_t* a_scales, const int32_t* a_rows,
+                           const int32_t* offsets, const void* packed, int which, int epilogue, void* c,
+                           int c_dtype, uint8_t* c_scales, void* stream);
+
+/* Bytes of scratch memory moe_layer_mxfp8() needs (host-only, no HIP call). */
+size_t moe_layer_workspace_bytes_mxfp8(const moe_shape* s);
+
+/*
+ * moe_layer_mxfp8 -- moe_layer() with MXFP8 expert GEMMs: routing and
+ * dispatch from the unquantised x exactly as moe_layer; each token row
+ * quantised once along H; gate/up on the scaled MFMA with the SwiGLU epilogue
+ * writing h as MXFP8; down on the scaled MFMA writing fp16 expert outputs;
+ * combine as moe_layer.  Same arguments as moe_layer(), with packed from
+ * moe_pack_weights_mxfp8() and ws of moe_layer_workspace_bytes_mxfp8(s) bytes.
+ */
+int moe_layer_mxfp8(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
+                    const float* bias, const void* packed, float* out,
+                    int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                    int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_layer_noalloc -- moe_layer() for callers that cannot allocate device

@@ -29,6 +29,7 @@ MOE_ERR_HIP = -4
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_F16 = 2
+MOE_MXFP8 = 3
 
 MOE_GEMM_GATE_UP = 0
 MOE_GEMM_DOWN = 1
@@ -42,6 +43,8 @@ EXPORTED = [
     "moe_pack_weights", "moe_route", "moe_route_from_logits", "moe_dispatch", "moe_grouped_gemm",
     "moe_combine", "moe_layer", "moe_status_string", "moe_last_hip_error",
     "moe_probe_mfma_bf16_flops", "moe_probe_mfma_bf16", "moe_layer_noalloc",
+    "moe_packed_weight_bytes_mxfp8", "moe_pack_weights_mxfp8", "moe_quantize_mxfp8", "moe_grouped_gemm_mxfp8",
+    "moe_layer_workspace_bytes_mxfp8", "moe_layer_mxfp8",
 ]
 
 MOE_LAYER_NOALLOC_MAX_WS_BYTES = 64 << 20
@@ -127,6 +130,12 @@ def load() -> ctypes.CDLL:
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_last_hip_error": (ctypes.c_int32, []),
         "moe_layer_noalloc": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_packed_weight_bytes_mxfp8": (sz, [_S]),
+        "moe_pack_weights_mxfp8": (i32, [_S, _P, _P, _P, i32, _P, _P]),
+        "moe_quantize_mxfp8": (i32, [ctypes.c_int64, ctypes.c_int32, _P, i32, _P, _P, _P]),
+        "moe_grouped_gemm_mxfp8": (i32, [_S, _P, _P, _P, _P, _P, i32, i32, _P, i32, _P, _P]),
+        "moe_layer_workspace_bytes_mxfp8": (sz, [_S]),
+        "moe_layer_mxfp8": (i32, [_S, _P, i32, _P, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "moe_probe_mfma_bf16_flops": (ctypes.c_int64, [i32, i32]),
         "moe_probe_mfma_bf16": (i32, [i32, i32, _P, _P]),
     }
@@ -399,3 +408,101 @@ def moe_probe_mfma_bf16(blocks: int, iters: int, sink: torch.Tensor, stream=None
     st = load().moe_probe_mfma_bf16(blocks, iters, _ptr(sink, torch.float32, None, "sink"), _stream(stream))
     _check("moe_probe_mfma_bf16", st)
     return int(load().moe_probe_mfma_bf16_flops(blocks, iters))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (OCP microscaling, E4M3 codes + E8M0 scale per 32 along K)
+# ---------------------------------------------------------------------------
+
+def moe_packed_weight_bytes_mxfp8(s: Shape) -> int:
+    return int(load().moe_packed_weight_bytes_mxfp8(ctypes.byref(s.c())))
+
+
+def moe_pack_weights_mxfp8(s: Shape, w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                           packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    n = s.E_loc * s.H * s.I
+    dt = w_gate.dtype
+    need = moe_packed_weight_bytes_mxfp8(s)
+    if need == 0:
+        raise MoeError("moe_packed_weight_bytes_mxfp8", MOE_ERR_UNSUPPORTED, 0, "shape not supported for MXFP8")
+    if packed is None:
+        packed = _empty(need, torch.uint8, w_gate.device)
+    st = load().moe_pack_weights_mxfp8(ctypes.byref(s.c()), _ptr(w_gate, dt, n, "w_gate"), _ptr(w_up, dt, n, "w_up"),
+                                       _ptr(w_down, dt, n, "w_down"), _dt(w_gate),
+                                       _ptr(packed, torch.uint8, None, "packed"), _stream(stream))
+    _check("moe_pack_weights_mxfp8", st)
+    return packed
+
+
+def moe_quantize_mxfp8(x: torch.Tensor, codes=None, scales=None, stream=None):
+    """x [rows, K] bf16/fp32 -> (codes uint8 [rows, K], scales uint8 [rows, K/32])."""
+    rows, K = x.shape
+    if codes is None:
+        codes = _empty((rows, K), torch.uint8, x.device)
+    if scales is None:
+        scales = _empty((rows, K // 32), torch.uint8, x.device)
+    st = load().moe_quantize_mxfp8(rows, K, _ptr(x, None, rows * K, "x"), _dt(x),
+                                   _ptr(codes, torch.uint8, rows * K, "codes"),
+                                   _ptr(scales, torch.uint8, rows * (K // 32), "scales"), _stream(stream))
+    _check("moe_quantize_mxfp8", st)
+    return codes, scales
+
+
+def moe_grouped_gemm_mxfp8(s: Shape, a: torch.Tensor, a_scales: torch.Tensor, offsets: torch.Tensor,
+                           packed: torch.Tensor, which: int, epilogue: int = MOE_EPI_NONE, c=None,
+                           c_dtype=torch.float16, c_scales=None, a_rows=None, stream=None):
+    """MXFP8 grouped GEMM.  c_dtype torch.uint8 means MXFP8 output (SwiGLU only):
+    returns (codes [cap, I], scales [cap, I/32]); otherwise returns c."""
+    cap = s.cap
+    kd = s.H if which == MOE_GEMM_GATE_UP else s.I
+    if which == MOE_GEMM_GATE_UP:
+        nc = s.I if epilogue == MOE_EPI_SWIGLU else 2 * s.I
+    else:
+        nc = s.H
+    mx_out = c_dtype == torch.uint8
+    if c is None:
+        c = _empty((cap, nc), c_dtype, a.device)
+    if mx_out and c_scales is None:
+        c_scales = _empty((cap, nc // 32), torch.uint8, a.device)
+    if a.numel() % kd or a_scales.numel() * 32 != a.numel():
+        raise ValueError("a [rows, K] codes with a_scales [rows, K/32]")
+    st = load().moe_grouped_gemm_mxfp8(ctypes.byref(s.c()), _ptr(a, torch.uint8, None, "a"),
+                                       _ptr(a_scales, torch.uint8, None, "a_scales"),
+                                       _ptr(a_rows, torch.int32, cap, "a_rows"),
+                                       _ptr(offsets, torch.int32, s.E_loc + 1, "offsets"),
+                                       _ptr(packed, torch.uint8, None, "packed"), which, epilogue,
+                                       _ptr(c, None, cap * nc, "c"), MOE_MXFP8 if mx_out else _dt(c),
+                                       _ptr(c_scales, torch.uint8, None, "c_scales") if mx_out else None,
+                                       _stream(stream))
+    _check("moe_grouped_gemm_mxfp8", st)
+    return (c, c_scales) if mx_out else c
+
+
+def moe_layer_workspace_bytes_mxfp8(s: Shape) -> int:
+    return int(load().moe_layer_workspace_bytes_mxfp8(ctypes.byref(s.c())))
+
+
+def moe_layer_mxfp8(s: Shape, x: torch.Tensor, w_router: torch.Tensor, packed: torch.Tensor,
+                    bias: Optional[torch.Tensor] = None, out=None, ws=None, *, topk_idx=None, topk_w=None,
+                    counts=None, offsets=None, row_token=None, row_slot=None, slot_row=None,
+                    stream=None) -> torch.Tensor:
+    """The layer share with MXFP8 expert GEMMs (packed from moe_pack_weights_mxfp8)."""
+    if out is None:
+        out = _empty((s.T, s.H), torch.float32, x.device)
+    if ws is None:
+        ws = _empty(max(moe_layer_workspace_bytes_mxfp8(s), 16), torch.uint8, x.device)
+    cap = s.cap
+    st = load().moe_layer_mxfp8(ctypes.byref(s.c()), _ptr(x, None, s.T * s.H, "x"), _dt(x),
+                                _ptr(w_router, None, s.H * s.E, "w_router"), _dt(w_router),
+                                _ptr(bias, torch.float32, s.E, "bias"), _ptr(packed, torch.uint8, None, "packed"),
+                                _ptr(out, torch.float32, s.T * s.H, "out"),
+                                _ptr(topk_idx, torch.int32, s.T * s.K, "topk_idx"),
+                                _ptr(topk_w, torch.float32, s.T * s.K, "topk_w"),
+                                _ptr(counts, torch.int32, s.E_loc, "counts"),
+                                _ptr(offsets, torch.int32, s.E_loc + 1, "offsets"),
+                                _ptr(row_token, torch.int32, cap, "row_token"),
+                                _ptr(row_slot, torch.int32, cap, "row_slot"),
+                                _ptr(slot_row, torch.int32, s.T * s.K, "slot_row"),
+                                _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check("moe_layer_mxfp8", st)
+    return out

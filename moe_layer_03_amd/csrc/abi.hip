@@ -123,6 +123,65 @@ LayerWs carve_layer(const moe_shape& s, void* base) {
     return w;
 }
 
+// Workspace of moe_layer_mxfp8, in carve order.
+struct MxLayerWs {
+    int32_t* topk_idx;
+    float* topk_w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* row_token;
+    int32_t* row_slot;
+    int32_t* slot_row;
+    void* dispatch_scratch;
+    void* route_scratch;
+    size_t route_bytes;
+    uint8_t* x_codes;   // [T][H]
+    uint8_t* x_scales;  // [T][H/32]
+    uint8_t* h_codes;   // [cap][I]
+    uint8_t* h_scales;  // [cap][I/32]
+    uint16_t* y;        // [cap][H] fp16
+    size_t bytes;
+};
+
+MxLayerWs carve_layer_mx(const moe_shape& s, void* base) {
+    const size_t TK = static_cast<size_t>(s.T) * s.K;
+    const size_t E_loc = static_cast<size_t>(s.e_end - s.e_begin);
+    const size_t cap = static_cast<size_t>(cap_rows(s));
+    const size_t T = static_cast<size_t>(s.T);
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* r = p ? p + off : nullptr;
+        off += align256(bytes);
+        return r;
+    };
+    MxLayerWs w;
+    w.topk_idx = reinterpret_cast<int32_t*>(take(TK * 4));
+    w.topk_w = reinterpret_cast<float*>(take(TK * 4));
+    w.counts = reinterpret_cast<int32_t*>(take(E_loc * 4));
+    w.offsets = reinterpret_cast<int32_t*>(take((E_loc + 1) * 4));
+    w.row_token = reinterpret_cast<int32_t*>(take(cap * 4));
+    w.row_slot = reinterpret_cast<int32_t*>(take(cap * 4));
+    w.slot_row = reinterpret_cast<int32_t*>(take(TK * 4));
+    w.dispatch_scratch = take(dispatch_scratch_bytes(s));
+    w.route_bytes = route_screen_bytes(s, MOE_BF16, MOE_BF16);
+    w.route_scratch = take(w.route_bytes);
+    w.x_codes = reinterpret_cast<uint8_t*>(take(T * s.H));
+    w.x_scales = reinterpret_cast<uint8_t*>(take(T * s.H / 32));
+    w.h_codes = reinterpret_cast<uint8_t*>(take(cap * s.I));
+    w.h_scales = reinterpret_cast<uint8_t*>(take(cap * s.I / 32));
+    w.y = reinterpret_cast<uint16_t*>(take(cap * s.H * 2));
+    w.bytes = off;
+    return w;
+}
+
+// MXFP8 calls: H and I multiples of 256 (whole 64-k steps in groups of four).
+int check_mx_shape(const moe_shape* s) {
+    MOE_TRY(check_shape(s));
+    if (s->H % 256 != 0 || s->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 }  // namespace
 
 void set_last_hip_error(hipError_t e) { g_last_hip_error = static_cast<int32_t>(e); }
@@ -301,6 +360,97 @@ int moe_layer(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
                                     MOE_F16, st));
     }
     MOE_TRY(launch_grouped_gemm(*s, w.h, MOE_F16, nullptr, off, pk, MOE_GEMM_DOWN, MOE_EPI_NONE, w.y, MOE_F16, st));
+    MOE_TRY(launch_combine(*s, w.y, MOE_F16, sr, tw, out, st));
+    return MOE_OK;
+}
+
+size_t moe_packed_weight_bytes_mxfp8(const moe_shape* s) {
+    if (check_mx_shape(s) != MOE_OK) return 0;
+    return mx_packed_weight_bytes(*s);
+}
+
+int moe_pack_weights_mxfp8(const moe_shape* s, const void* w_gate, const void* w_up, const void* w_down, int dtype,
+                           void* packed, void* stream) {
+    MOE_TRY(check_mx_shape(s));
+    if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+    if (!ok16(w_gate) || !ok16(w_up) || !ok16(w_down) || !ok16(packed)) return MOE_ERR_INVALID_ARG;
+    return launch_mx_pack_weights(*s, w_gate, w_up, w_down, dtype, static_cast<uint8_t*>(packed),
+                                  static_cast<hipStream_t>(stream));
+}
+
+int moe_quantize_mxfp8(int64_t rows, int32_t K, const void* x, int x_dtype, uint8_t* codes, uint8_t* scales,
+                       void* stream) {
+    if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
+    if (!dtype_ok(x_dtype)) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!ok16(x) || !ok16(codes) || scales == nullptr) return MOE_ERR_INVALID_ARG;
+    return launch_mx_quantize(rows, K, x, x_dtype, codes, scales, static_cast<hipStream_t>(stream));
+}
+
+int moe_grouped_gemm_mxfp8(const moe_shape* s, const uint8_t* a, const uint8_t* a_scales, const int32_t* a_rows,
+                           const int32_t* offsets, const void* packed, int which, int epilogue, void* c, int c_dtype,
+                           uint8_t* c_scales, void* stream) {
+    MOE_TRY(check_mx_shape(s));
+    if (which != MOE_GEMM_GATE_UP && which != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARG;
+    if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU) return MOE_ERR_INVALID_ARG;
+    if (which == MOE_GEMM_DOWN && epilogue != MOE_EPI_NONE) return MOE_ERR_INVALID_ARG;
+    if (!out_dtype_ok(c_dtype) && !(c_dtype == MOE_MXFP8 && epilogue == MOE_EPI_SWIGLU)) return MOE_ERR_UNSUPPORTED;
+    if (s->T == 0) return MOE_OK;
+    if (!ok16(a) || a_scales == nullptr || !opt4(a_rows) || !ok4(offsets) || !ok16(packed) || !ok16(c))
+        return MOE_ERR_INVALID_ARG;
+    if (c_dtype == MOE_MXFP8 && c_scales == nullptr) return MOE_ERR_INVALID_ARG;
+    return launch_mx_grouped_gemm(*s, a, a_scales, a_rows, offsets, static_cast<const uint8_t*>(packed), which,
+                                  epilogue, c, c_dtype, c_scales, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_layer_workspace_bytes_mxfp8(const moe_shape* s) {
+    if (check_mx_shape(s) != MOE_OK) return 0;
+    return carve_layer_mx(*s, nullptr).bytes;
+}
+
+int moe_layer_mxfp8(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
+                    const float* bias, const void* packed, float* out, int32_t* topk_idx, float* topk_w,
+                    int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
+                    void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_mx_shape(s));
+    if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype)) return MOE_ERR_UNSUPPORTED;
+    if (x_dtype != w_dtype) return MOE_ERR_UNSUPPORTED;
+    if (!opt4(topk_idx) || !opt4(topk_w) || !opt4(counts) || !opt4(offsets) || !opt4(row_token) ||
+        !opt4(row_slot) || !opt4(slot_row))
+        return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < carve_layer_mx(*s, nullptr).bytes) return MOE_ERR_WORKSPACE;
+    if (!ok16(ws)) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MxLayerWs w = carve_layer_mx(*s, ws);
+    int32_t* cnt = counts ? counts : w.counts;
+    int32_t* off = offsets ? offsets : w.offsets;
+    if (s->T == 0) {
+        if (counts == nullptr && offsets == nullptr) return MOE_OK;
+        return launch_dispatch(*s, nullptr, nullptr, x_dtype, cnt, off, nullptr, nullptr, nullptr, nullptr,
+                               w.dispatch_scratch, st);
+    }
+    if (!ok16(x) || !ok16(w_router) || !ok16(packed) || !ok16(out) || !opt4(bias)) return MOE_ERR_INVALID_ARG;
+    int32_t* idx = topk_idx ? topk_idx : w.topk_idx;
+    float* tw = topk_w ? topk_w : w.topk_w;
+    int32_t* rt = row_token ? row_token : w.row_token;
+    int32_t* rs = row_slot ? row_slot : w.row_slot;
+    int32_t* sr = slot_row ? slot_row : w.slot_row;
+    const uint8_t* pk = static_cast<const uint8_t*>(packed);
+    // few rows per expert: the router's idle CUs read the gate/up weight codes into the last-level cache
+    CachePrefetch pf;
+    const size_t gu_bytes = mx_packed_gate_up_code_bytes(*s);
+    if (mx_gemm_streams_weights(*s) && gu_bytes <= kLastLevelCacheBytes) {
+        pf.region = pk;
+        pf.bytes = gu_bytes;
+    }
+    MOE_TRY(launch_route_prefetch(*s, x, x_dtype, w_router, bias, idx, tw, nullptr, w.route_scratch, w.route_bytes,
+                                  st, pf));
+    MOE_TRY(launch_mx_quantize(s->T, s->H, x, x_dtype, w.x_codes, w.x_scales, st));
+    MOE_TRY(launch_dispatch(*s, idx, nullptr, x_dtype, cnt, off, rt, rs, sr, nullptr, w.dispatch_scratch, st));
+    MOE_TRY(launch_mx_grouped_gemm(*s, w.x_codes, w.x_scales, rt, off, pk, MOE_GEMM_GATE_UP, MOE_EPI_SWIGLU,
+                                   w.h_codes, MOE_MXFP8, w.h_scales, st));
+    MOE_TRY(launch_mx_grouped_gemm(*s, w.h_codes, w.h_scales, nullptr, off, pk, MOE_GEMM_DOWN, MOE_EPI_NONE, w.y,
+                                   MOE_F16, nullptr, st));
     MOE_TRY(launch_combine(*s, w.y, MOE_F16, sr, tw, out, st));
     return MOE_OK;
 }

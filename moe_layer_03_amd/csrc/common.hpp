@@ -150,4 +150,18 @@ int launch_gate_up_deriving_dispatch(const moe_shape& s, const uint16_t* x, cons
 int launch_combine(const moe_shape& s, const void* y_packed, int y_dtype, const int32_t* slot_row,
                    const float* topk_w, float* out, hipStream_t st);
 
+// MXFP8 (mxfp8.hip)
+size_t mx_packed_gate_up_code_bytes(const moe_shape& s);
+size_t mx_packed_down_code_bytes(const moe_shape& s);
+size_t mx_packed_weight_bytes(const moe_shape& s);
+int launch_mx_pack_weights(const moe_shape& s, const void* w_gate, const void* w_up, const void* w_down, int dtype,
+                           uint8_t* packed, hipStream_t st);
+int launch_mx_quantize(int64_t rows, int K, const void* x, int x_dtype, uint8_t* codes, uint8_t* scales,
+                       hipStream_t st);
+// Whether launch_mx_grouped_gemm takes its weight-streaming form.
+bool mx_gemm_streams_weights(const moe_shape& s);
+int launch_mx_grouped_gemm(const moe_shape& s, const uint8_t* a, const uint8_t* a_scales, const int32_t* a_rows,
+                           const int32_t* offsets, const uint8_t* packed, int which, int epilogue, void* c,
+                           int c_dtype, uint8_t* c_scales, hipStream_t st);
+
 }  // namespace moe
