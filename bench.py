@@ -22,7 +22,8 @@ skewed prefill, whole layer) are measured the same way afterwards and
 reported under ``configs`` (the decode shard under ``decode``), followed by
 the grouped-GEMM micro-benchmark of a decode rank: every local expert
 activated by one token, for 32, 16, 8, 4 and 2 local experts
-(``gemm_single_token_sweep``).  The
+(``gemm_single_token_sweep``), and the prefill and decode shards with MXFP8
+expert GEMMs (``mxfp8``: the quantisation the pages deploy).  The
 line also carries the MFMA and copy rates measured on this chip next to the
 published peaks, and the oracle timed on the host cores (headline workload).
 Prints one JSON line.
@@ -40,6 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16/fp16 MFMA (published)
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (prefill) / % HBM GB/s (decode), 1 GPU"
@@ -315,6 +317,121 @@ def measure(wl, steps, warmup, graph, copy_probe_mib=0):
     return res, inp
 
 
+def measure_mxfp8(wl, steps, warmup):
+    """The layer share with MXFP8 expert GEMMs (moe_layer_mxfp8): fused steps with a HIP event per step, then
+    the staged calls with events around route, activation quantisation, dispatch, gate/up, down and combine."""
+    import numpy as np
+    import torch
+
+    from moe_layer_03_amd import binding as B
+    from moe_layer_03_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    s = B.Shape.of(wl)
+    inp = W.make_inputs(wl)
+
+    def dev_t(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+    x, wr = dev_t(inp.x), dev_t(inp.w_router)
+    bias = dev_t(inp.bias) if inp.bias is not None else None
+    g, u, d = dev_t(inp.w_gate), dev_t(inp.w_up), dev_t(inp.w_down)
+    packed = B.moe_pack_weights_mxfp8(s, g, u, d)
+    torch.cuda.synchronize()
+    del g, u, d, inp
+    ws = torch.empty(max(B.moe_layer_workspace_bytes_mxfp8(s), 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device=dev)
+    cap = s.cap
+    i32 = torch.int32
+    b = dict(idx=torch.empty((s.T, s.K), dtype=i32, device=dev), tw=torch.empty((s.T, s.K), dtype=torch.float32,
+                                                                               device=dev),
+             xc=torch.empty((s.T, s.H), dtype=torch.uint8, device=dev),
+             xs=torch.empty((s.T, s.H // 32), dtype=torch.uint8, device=dev),
+             hc=torch.empty((cap, s.I), dtype=torch.uint8, device=dev),
+             hs=torch.empty((cap, s.I // 32), dtype=torch.uint8, device=dev),
+             y=torch.empty((cap, s.H), dtype=torch.float16, device=dev),
+             out=torch.empty((s.T, s.H), dtype=torch.float32, device=dev),
+             ws_route=torch.empty(max(B.moe_route_workspace_bytes(s), 16), dtype=torch.uint8, device=dev),
+             ws_d=torch.empty(max(B.moe_dispatch_workspace_bytes(s), 16), dtype=torch.uint8, device=dev))
+    stages = ["route", "quantize_x", "dispatch", "gemm_gate_up", "gemm_down", "combine"]
+    dd = {}
+
+    def staged(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        B.moe_route(s, x, wr, bias, topk_idx=b["idx"], topk_w=b["tw"], ws=b["ws_route"])
+        mark(1)
+        B.moe_quantize_mxfp8(x, b["xc"], b["xs"])
+        mark(2)
+        dd.update(B.moe_dispatch(s, b["idx"], None, ws=b["ws_d"]))
+        mark(3)
+        B.moe_grouped_gemm_mxfp8(s, b["xc"], b["xs"], dd["offsets"], packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_SWIGLU,
+                                 c=b["hc"], c_dtype=torch.uint8, c_scales=b["hs"], a_rows=dd["row_token"])
+        mark(4)
+        B.moe_grouped_gemm_mxfp8(s, b["hc"], b["hs"], dd["offsets"], packed, B.MOE_GEMM_DOWN, B.MOE_EPI_NONE,
+                                 c=b["y"])
+        mark(5)
+        B.moe_combine(s, b["y"], dd["slot_row"], b["tw"], out=b["out"])
+        mark(6)
+
+    def fused():
+        B.moe_layer_mxfp8(s, x, wr, packed, bias, out=out, ws=ws)
+
+    for _ in range(warmup):
+        fused()
+        staged()
+    torch.cuda.synchronize()
+    ev_f = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev_f[k].record()
+        fused()
+    ev_f[steps].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = np.array([ev_f[k].elapsed_time(ev_f[k + 1]) for k in range(steps)])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for k in range(steps):
+        staged(evs[k])
+    torch.cuda.synchronize()
+    stage_ms = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
+                for i, nm in enumerate(stages)}
+    counts = dd["counts"].cpu().numpy()
+    n_loc = int(dd["offsets"][-1].item())
+    H, I, E, T = wl.H, wl.I, wl.E, wl.T
+    active = int((counts > 0).sum())
+    flops = 2 * T * H * E + n_loc * (2 * H * 2 * I + 2 * I * H)
+    wbytes = active * 3 * H * I * (1 + 1 / 32)          # fp8 codes + one scale byte per 32
+    bytes_alg = wbytes + H * E * 2 + T * H * 2 + T * H * 4
+    gu_flops = n_loc * 2 * H * 2 * I
+    gu_bytes = active * 2 * H * I * (1 + 1 / 32) + n_loc * H * (1 + 1 / 32) + n_loc * I * (1 + 1 / 32)
+    t_gu = stage_ms["gemm_gate_up"] * 1e-3
+    if gu_flops / gu_bytes >= PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        ach = gu_flops / t_gu / 1e12
+        roof = dict(kernel="grouped_gemm_mx_kernel (gate/up, scaled fp8 MFMA)", bound="mfma", achieved=round(ach, 2),
+                    peak=PEAK_FP8_TFLOPS, unit="TFLOP/s", frac=round(ach / PEAK_FP8_TFLOPS, 4),
+                    per_launch=dict(flops=gu_flops, us=round(t_gu * 1e6, 2)))
+    else:
+        ach = gu_bytes / t_gu / 1e9
+        roof = dict(kernel="grouped_gemm_mx_skinny_kernel (gate/up, scaled fp8 MFMA)", bound="hbm",
+                    achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4),
+                    per_launch=dict(bytes=int(gu_bytes), us=round(t_gu * 1e6, 2)))
+    sec = ms * 1e-3
+    res = {"workload": wl.name, "steps": steps, "ms_per_step": round(ms, 4),
+           "ms_median": round(float(np.median(per)), 4), "ms_min": round(float(per.min()), 4),
+           "tokens_s": round(T / sec, 1), "tflops": round(flops / sec / 1e12, 2),
+           "mfma_frac_fp8_peak": round(flops / sec / 1e12 / PEAK_FP8_TFLOPS, 4),
+           "gbs": round(bytes_alg / sec / 1e9, 1), "hbm_frac": round(bytes_alg / sec / 1e9 / PEAK_HBM_GBS, 4),
+           "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}, "roofline": roof,
+           "fused_entry_bitwise_equal": bool(torch.equal(out, b["out"]))}
+    del packed, ws, out, b, x, wr
+    torch.cuda.empty_cache()
+    return res
+
+
 def gemm_single_token_sweep(e_locs=(32, 16, 8, 4, 2), reps=50, warmup=20):
     """The grouped expert GEMMs (gate/up with SwiGLU, then down) with every local expert activated by exactly
     one token, for several local-expert counts: the GEMM micro-benchmark of one expert-parallel decode rank.
@@ -408,6 +525,13 @@ def main():
             configs[name] = r
             print(f"[bench] {name}: {r['ms_per_step']} ms/step", file=sys.stderr, flush=True)
 
+    mxfp8 = None
+    if not args.only:
+        mxfp8 = {}
+        for name in ("prefill_ep4_shard", "decode_ep16_shard"):
+            mxfp8[name] = measure_mxfp8(W.WORKLOADS[name], args.steps, args.warmup)
+            print(f"[bench] mxfp8 {name}: {mxfp8[name]['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+
     sweep = None
     if not args.only:
         sweep = gemm_single_token_sweep()
@@ -451,6 +575,7 @@ def main():
         "decode": configs.get("decode_ep16_shard"),
         "configs": {k: v for k, v in configs.items() if k != wl.name},
         "gemm_single_token_sweep": sweep,
+        "mxfp8": mxfp8,
         "peaks": {"spec_bf16_tflops": PEAK_BF16_TFLOPS, "spec_hbm_gbs": PEAK_HBM_GBS,
                   **(peaks or {})},
         "host_cpu": host_cpu_model(),
