@@ -181,13 +181,7 @@ struct MxArgs {
     int E_loc, N, Kd, ldc, I;
 };
 
-// One 4-byte-per-lane buffer -> LDS copy (lane l lands at base + 4 l).
-__device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_wave_base, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_wave_base)),
-        4, static_cast<int>(voff), 0, 0, 0);
-}
-// One 16-byte-per-lane buffer -> LDS copy.
+// One 16-byte-per-lane buffer -> LDS copy (lane l lands at base + 16 l).
 __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_wave_base, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_wave_base)),
@@ -218,10 +212,14 @@ template <> struct MxOutType<kMxOutMX> { typedef uint8_t type; };
 // [n-tile][m-tile], contiguous per XCD; a tile of two 128-row slabs x 256
 // columns; each wave 128 rows x 64 columns (4 x 2 MFMA tiles of 32 x 32, 128
 // float32 accumulators per lane) -- with one 64-k step per LDS stage: 64-byte
-// code rows of A (XOR-swizzled granules), 2 KiB code tiles of B, and the
-// stage's scale bytes (4 per A row and per B column, the two blocks of this
-// step and of the next), all by direct buffer -> LDS copies into a ring of NB
-// stages; rows past the segment read zeros (no memory traffic).
+// code rows of A (XOR-swizzled granules) and 2 KiB code tiles of B, by direct
+// buffer -> LDS copies into a ring of NB stages; rows past the segment read
+// zeros (no memory traffic).  Scales travel apart from the codes, 16 bytes
+// (16 blocks: 8 k-steps) per A row and per B column in one copy per thread
+// every 8 k-steps, into two alternating scale buffers: the scales are spread
+// one row or column per lane, so fewer, wider copies cut the cache lines each
+// copy touches 8-fold.  A K that is not a multiple of 512 ends in a half group,
+// whose copy starts 8 blocks early so it never reads past a row; K >= 512.
 // ---------------------------------------------------------------------------
 template <int MODE, int OUT, int NB>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
@@ -230,14 +228,16 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
     constexpr int NWAVES = 8, NTHREADS = 512, WN = 4, BM = 128, UM = 256, BN = 256, TM = 4;
     constexpr int A_STAGE = UM * 64;                  // bytes
     constexpr int B_STAGE = BN * 64;
-    constexpr int S_STAGE = (UM + BN) * 4;            // scale bytes: 4 per A row, 4 per B column
     constexpr int A_DMA = A_STAGE / 16 / NTHREADS;    // 2
     constexpr int B_DMA = B_STAGE / 16 / NTHREADS;    // 2
-    constexpr int LOADS = A_DMA + B_DMA + 1;          // plus one 4-byte scale copy
-    static_assert(A_DMA == 2 && B_DMA == 2 && S_STAGE == 4 * NTHREADS, "stage split");
+    constexpr int LOADS = A_DMA + B_DMA;              // copies per thread per stage
+    constexpr int SG = 8;                             // k-steps per scale group
+    constexpr int S_GROUP = (UM + BN) * 16;           // scale bytes of a group: 16 per A row and per B column
+    static_assert(NB == 4 && A_DMA == 2 && B_DMA == 2 && UM + BN == NTHREADS, "stage split");
+    static_assert(SG % NB == 0, "a scale group spans whole turns of the ring");
     __shared__ __attribute__((aligned(1024))) uint8_t s_a[NB][A_STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t s_b[NB][B_STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t s_s[NB][S_STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][S_GROUP];
     __shared__ int s_mt[kMaxExperts + 1];
     __shared__ int s_tmp[NWAVES];
 
@@ -310,13 +310,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
             const int64_t tl = (static_cast<int64_t>(e) * (p.N >> 6) + n_tile * WN + q) * nk * 2 + t;   // k-step 0
             b_off[d] = static_cast<uint32_t>(tl * kMxTile + part * 1024 + lane * 16);
         }
-        // scale copy: threads 0..255 the A rows of the tile, 256..511 its B columns; 4 bytes = blocks
-        // 4m .. 4m+3 of the row or column, m = k-step / 2 (this step's two blocks and the other
-        // step of the pair)
+        // scale copies: threads 0..255 the A rows of the tile, 256..511 its B columns (thread t's
+        // 16 bytes land at record t of the group buffer); the split falls on a wave boundary and is
+        // taken on the wave index, so the descriptor stays in scalar registers
+        const bool a_side = wave < UM / kWave;
+        const __amdgpu_buffer_rsrc_t s_rsrc = a_side ? as_rsrc : bs_rsrc;
         uint32_t s_off;
-        __amdgpu_buffer_rsrc_t s_rsrc;
-        if (tid < UM) {
-            s_rsrc = as_rsrc;
+        if (a_side) {
             s_off = kOutOfRange;
             if (tid < rows_valid) {
                 const int r = row0 + tid;
@@ -324,7 +324,6 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
                 s_off = static_cast<uint32_t>(src * kb32);
             }
         } else {
-            s_rsrc = bs_rsrc;
             s_off = static_cast<uint32_t>((static_cast<int64_t>(e) * p.N + n_tile * BN + (tid - UM)) * kb32);
         }
         auto issue = [&](int kt, int st) {
@@ -334,7 +333,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
 #pragma unroll
             for (int d = 0; d < B_DMA; ++d)
                 copy16_to_lds(b_rsrc, &s_b[st][(wave * B_DMA + d) * 1024], b_off[d] + kt * 2 * kMxTile);
-            copy4_to_lds(s_rsrc, &s_s[st][wave * 256], s_off + (kt >> 1) * 4);
+        };
+        // scale group g covers k-steps 8g .. 8g+7, blocks 16g .. 16g+15; its copy starts at block
+        // b0(g) = min(16 g, Kd/32 - 16), so a k-step's byte in a record is 2 kt + h - b0(g)
+        const int ng = (nk + SG - 1) / SG;
+        auto group_b0 = [&](int g) { return min(16 * g, kb32 - 16); };
+        auto issue_scales = [&](int buf, int g) {
+            copy16_to_lds(s_rsrc, &s_sc[buf][wave * 1024], s_off + static_cast<uint32_t>(group_b0(g)));
         };
 
         floatx16 acc[TM][2];
@@ -345,64 +350,96 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+        issue_scales(0, 0);
 #pragma unroll
         for (int q = 0; q + 1 < NB; ++q) issue(min(q, nk - 1), q);
 
         auto kloop = [&](auto nac) {
             constexpr int NA = decltype(nac)::value;
             // fragments of one k-step: A 2 x 16 bytes per row tile, B 2 x 16 bytes per column tile,
-            // and the lane's scale bytes (row / column lane & 31, block h of the step).  One set of
-            // registers: the next stage's fragments are read right after this stage's MFMAs issue
-            // (the second wave of the SIMD covers the LDS latency).
-            u32x4 fa[TM][2], fb[2][2];
-            uint32_t sa[TM], sb[2];
-            // the parity of k-step kt is compile-time: the k-loop is unrolled over the NB stages and
-            // k-step kt always sits in stage kt % NB (NB even)
-            auto read_frags = [&](int st, int par) {
-                const int sb_byte = (par << 1) + h;
-#pragma unroll
-                for (int i = 0; i < NA; ++i) {
-                    const int row = mh * BM + i * 32 + (lane & 31);
-                    const int sw = (row >> 2) & 3;
-                    fa[i][0] = *reinterpret_cast<const u32x4*>(&s_a[st][row * 64 + ((h ^ sw) << 4)]);
-                    fa[i][1] = *reinterpret_cast<const u32x4*>(&s_a[st][row * 64 + (((2 + h) ^ sw) << 4)]);
-                    sa[i] = s_s[st][row * 4 + sb_byte];
-                }
+            // and the lane's scale bytes (row / column lane & 31, block h of the step).  B fragments
+            // are double-buffered: the next stage's are read first, while this stage's MFMAs run; A
+            // fragments are single: each row tile's are refilled right after its two MFMAs issue.
+            // The k-loop is unrolled over a scale group (8 k-steps, two turns of the ring), so ring
+            // stage, register buffer and the step's place in its group are compile-time.
+            u32x4 fa[TM][2], fb[2][2][2];
+            uint32_t sa[TM], sb[2][2];
+            const int a_rec = (mh * BM + (lane & 31)) * 16 + h;          // + i * 512: row tile i
+            const int b_rec = (UM + nq * 64 + (lane & 31)) * 16 + h;     // + t * 512: column tile t
+            auto sc_off = [&](int kt) {                                  // uniform part of a scale address
+                kt = min(kt, nk - 1);                                    // (the last step reads ahead of the end)
+                const int g = kt / SG;
+                return (g & 1) * S_GROUP + 2 * kt - group_b0(g);
+            };
+            auto read_a = [&](int i, int st, int so) {
+                const int row = mh * BM + i * 32 + (lane & 31);
+                const int sw = (row >> 2) & 3;
+                fa[i][0] = *reinterpret_cast<const u32x4*>(&s_a[st][row * 64 + ((h ^ sw) << 4)]);
+                fa[i][1] = *reinterpret_cast<const u32x4*>(&s_a[st][row * 64 + (((2 + h) ^ sw) << 4)]);
+                sa[i] = (&s_sc[0][0])[so + a_rec + i * 512];
+            };
+            auto read_b = [&](int buf, int st, int so) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    fb[t][0] = *reinterpret_cast<const u32x4*>(&s_b[st][((nq * 2 + t) * 2 + 0) * 1024 + lane * 16]);
-                    fb[t][1] = *reinterpret_cast<const u32x4*>(&s_b[st][((nq * 2 + t) * 2 + 1) * 1024 + lane * 16]);
-                    sb[t] = s_s[st][UM * 4 + (nq * 64 + t * 32 + (lane & 31)) * 4 + sb_byte];
+                    fb[buf][t][0] =
+                        *reinterpret_cast<const u32x4*>(&s_b[st][((nq * 2 + t) * 2 + 0) * 1024 + lane * 16]);
+                    fb[buf][t][1] =
+                        *reinterpret_cast<const u32x4*>(&s_b[st][((nq * 2 + t) * 2 + 1) * 1024 + lane * 16]);
+                    sb[buf][t] = (&s_sc[0][0])[so + b_rec + t * 512];
                 }
             };
-            auto mfmas = [&]() {
-#pragma unroll
-                for (int i = 0; i < NA; ++i)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-                        acc[i][t] = mfma_mx(fa[i][0], fa[i][1], sa[i], fb[t][0], fb[t][1], sb[t], acc[i][t]);
-            };
-            // one k-step per stage
-            auto step = [&](int kt, int st) {
-                wait_vmcnt<LOADS * (NB - 3)>();        // this thread's copies of stage kt + 1 have landed
+            // k-step kt, at place q of its scale group (compile-time)
+            auto step = [&](int kt, auto qc) {
+                constexpr int q = decltype(qc)::value;
+                constexpr int st = q % NB, buf = q & 1, nbuf = buf ^ 1, nst = (q + 1) % NB;
+                // this thread's copies of stage kt + 1 have landed (after the group copy issued at the
+                // group's first step, one more copy may still be in flight at its second)
+                wait_vmcnt<q == 1 ? LOADS + 1 : LOADS>();
                 __builtin_amdgcn_s_barrier();          // ... everyone's; nobody reads stage kt - 1 any more
+                if constexpr (q == 0) issue_scales((kt / SG + 1) & 1, min(kt / SG + 1, ng - 1));
                 issue(min(kt + NB - 1, nk - 1), (st + NB - 1) % NB);
                 if constexpr (NA > 0) {
-                    mfmas();
-                    read_frags((st + 1) % NB, (st + 1) & 1);
+                    const int so = sc_off(kt + 1);
+                    read_b(nbuf, nst, so);
+                    __builtin_amdgcn_sched_barrier(0);
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int i = 0; i < NA; ++i) {
+                        acc[i][0] = mfma_mx(fa[i][0], fa[i][1], sa[i], fb[buf][0][0], fb[buf][0][1], sb[buf][0],
+                                            acc[i][0]);
+                        acc[i][1] = mfma_mx(fa[i][0], fa[i][1], sa[i], fb[buf][1][0], fb[buf][1][1], sb[buf][1],
+                                            acc[i][1]);
+                        read_a(i, nst, so);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // the two MFMAs ...
+                        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // ... then the row tile's reads
+                    }
                 }
             };
-            wait_vmcnt<LOADS * (NB - 2)>();            // stage 0 has landed
+            wait_vmcnt<LOADS * (NB - 2)>();            // scale group 0 and stage 0 have landed
             __builtin_amdgcn_s_barrier();
-            if constexpr (NA > 0) read_frags(0, 0);
-            int kt0 = 0;
-            for (; kt0 + NB <= nk; kt0 += NB) {
+            if constexpr (NA > 0) {
+                const int so = sc_off(0);
+                read_b(0, 0, so);
 #pragma unroll
-                for (int q = 0; q < NB; ++q) step(kt0 + q, q);
+                for (int i = 0; i < NA; ++i) read_a(i, 0, so);
             }
-#pragma unroll
-            for (int q = 0; q + 1 < NB; ++q)
-                if (kt0 + q < nk) step(kt0 + q, q);
+            int kt0 = 0;
+            for (; kt0 + SG <= nk; kt0 += SG) {
+                step(kt0 + 0, IntC<0>{});
+                step(kt0 + 1, IntC<1>{});
+                step(kt0 + 2, IntC<2>{});
+                step(kt0 + 3, IntC<3>{});
+                step(kt0 + 4, IntC<4>{});
+                step(kt0 + 5, IntC<5>{});
+                step(kt0 + 6, IntC<6>{});
+                step(kt0 + 7, IntC<7>{});
+            }
+            if (kt0 < nk) {                            // nk % 8 == 4: the half group
+                step(kt0 + 0, IntC<0>{});
+                step(kt0 + 1, IntC<1>{});
+                step(kt0 + 2, IntC<2>{});
+                step(kt0 + 3, IntC<3>{});
+            }
         };
         switch (active ? na : 0) {
             case 4: kloop(IntC<4>{}); break;
@@ -745,7 +782,9 @@ int launch_mx_grouped_gemm(const moe_shape& s, const uint8_t* a, const uint8_t* 
     const int64_t nn = which == MOE_GEMM_GATE_UP ? 2 * s.I : s.H;
     if (static_cast<int64_t>(args.a_rows_bound) * kd + 64 > kBufferRange || E_loc * nn * kd + 4096 > kBufferRange)
         return MOE_ERR_UNSUPPORTED;
-    const bool skinny = mx_gemm_streams_weights(s) && kd % 256 == 0;
+    // the tiled form stages scales 16 blocks at a time and needs K >= 512; below that every launch
+    // takes the weight-streaming form, whatever the row count
+    const bool skinny = (mx_gemm_streams_weights(s) && kd % 256 == 0) || kd < 512;
     if (which == MOE_GEMM_GATE_UP) {
         args.b = gu;
         args.b_scales = gus;

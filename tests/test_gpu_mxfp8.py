@@ -73,13 +73,17 @@ def _int_activations(rng, rows, K):
     return codes, scales, MX.dequantize(codes, scales)
 
 
-@pytest.mark.parametrize("counts", [[300, 200, 150, 100, 0, 37], [1] * 32, [5, 0, 70, 3]],
-                         ids=["tiled", "one_token_per_expert", "weight_streaming"])
-def test_grouped_gemm_exact_integers(B, counts):
+@pytest.mark.parametrize("counts,H,I", [([300, 200, 150, 100, 0, 37], 512, 256),
+                                        ([300, 200, 150, 100, 0, 37], 768, 512),
+                                        ([1] * 32, 512, 256), ([5, 0, 70, 3], 512, 256)],
+                         ids=["tiled", "tiled_half_scale_group", "one_token_per_expert", "weight_streaming"])
+def test_grouped_gemm_exact_integers(B, counts, H, I):
     """Both problems, float32 output, bit-exact: the tiled form (many rows per
-    expert) and the weight-streaming form (few)."""
+    expert) and the weight-streaming form (few).  The tiled form stages scales
+    8 k-steps (K = 512) at a time: K = 512 is one whole group, K = 768 a whole
+    group and a half one; K = 256 (the down problem at I = 256) takes the
+    weight-streaming form whatever the rows."""
     rng = np.random.default_rng(41)
-    H, I = 512, 256
     E_loc, n = len(counts), int(sum(counts))
     s = B.Shape(n, H, E_loc, 1, I, 0, E_loc)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
