@@ -250,9 +250,10 @@ def moe_route(s: Shape, x: torch.Tensor, w_router: torch.Tensor, bias: Optional[
               topk_idx=None, topk_w=None, logits=None, want_logits=False, ws=None, screened=True, stream=None):
     """Returns (topk_idx int32 [T,K], topk_w fp32 [T,K], logits fp32 [T,E] or None).
 
-    ``screened=False`` passes no workspace, so every logit is evaluated in its
-    fma chain; with the default the library screens when the shape allows it
-    (the outputs are the same)."""
+    ``screened=False`` passes no workspace, so (without logits requested) the
+    library takes its per-token form; with the default it passes a workspace of
+    ``moe_route_workspace_bytes`` and the library screens large bf16 batches or
+    tiles small ones when the shape allows it (the outputs are the same)."""
     dev = x.device
     if topk_idx is None:
         topk_idx = _empty((s.T, s.K), torch.int32, dev)

@@ -114,7 +114,7 @@ LayerWs carve_layer(const moe_shape& s, void* base) {
     w.row_slot = reinterpret_cast<int32_t*>(take(cap * 4));
     w.slot_row = reinterpret_cast<int32_t*>(take(TK * 4));
     w.dispatch_scratch = take(dispatch_scratch_bytes(s));
-    w.route_bytes = route_screen_bytes(s, MOE_BF16, MOE_BF16);
+    w.route_bytes = route_workspace_bytes(s);
     w.route_scratch = take(w.route_bytes);
     w.x_packed = reinterpret_cast<uint16_t*>(take(cap * s.H * 2));
     w.h = reinterpret_cast<uint16_t*>(take(cap * s.I * 2));
@@ -164,7 +164,7 @@ MxLayerWs carve_layer_mx(const moe_shape& s, void* base) {
     w.row_slot = reinterpret_cast<int32_t*>(take(cap * 4));
     w.slot_row = reinterpret_cast<int32_t*>(take(TK * 4));
     w.dispatch_scratch = take(dispatch_scratch_bytes(s));
-    w.route_bytes = route_screen_bytes(s, MOE_BF16, MOE_BF16);
+    w.route_bytes = route_workspace_bytes(s);
     w.route_scratch = take(w.route_bytes);
     w.x_codes = reinterpret_cast<uint8_t*>(take(T * s.H));
     w.x_scales = reinterpret_cast<uint8_t*>(take(T * s.H / 32));
@@ -199,7 +199,7 @@ size_t moe_dispatch_workspace_bytes(const moe_shape* s) {
 
 size_t moe_route_workspace_bytes(const moe_shape* s) {
     if (check_shape(s) != MOE_OK) return 0;
-    return route_screen_bytes(*s, MOE_BF16, MOE_BF16);
+    return route_workspace_bytes(*s);
 }
 
 int moe_route_screen_layout(const moe_shape* s, int x_dtype, int w_dtype, moe_route_screen_info* info) {
@@ -235,7 +235,7 @@ int moe_route(const moe_shape* s, const void* x, int x_dtype, const void* w_rout
     if (x_dtype != w_dtype) return MOE_ERR_UNSUPPORTED;
     if (ws != nullptr) {
         if (!aligned(ws, 16)) return MOE_ERR_INVALID_ARG;
-        if (ws_bytes < route_screen_bytes(*s, x_dtype, w_dtype)) return MOE_ERR_WORKSPACE;
+        if (ws_bytes < route_workspace_bytes(*s)) return MOE_ERR_WORKSPACE;
     }
     if (s->T == 0) return MOE_OK;   // nothing to route; empty tensors may have null pointers
     if (!ok16(x) || !ok16(w_router) || !ok4(topk_idx) || !ok4(topk_w) || !opt4(bias) || !opt4(logits))

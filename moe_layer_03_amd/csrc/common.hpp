@@ -109,6 +109,9 @@ void set_last_hip_error(hipError_t e);
 // Launchers (defined in the kernel translation units).  Arguments are
 // validated by the entry points before these are called.
 size_t route_screen_bytes(const moe_shape& s, int x_dtype, int w_dtype);
+// Scratch bytes that let the router take its faster paths: the screened path
+// (large bf16 batches), or the tiled path's logits (small batches).
+size_t route_workspace_bytes(const moe_shape& s);
 // Where the screened path leaves its estimates in the workspace; false when
 // the shape and dtypes do not take that path.
 bool route_screen_layout(const moe_shape& s, int x_dtype, int w_dtype, moe_route_screen_info* info);

@@ -12,10 +12,13 @@
 // For E <= 128 a lane owns (token, expert) chains; activations and router
 // weights are staged per workgroup in LDS as float32 (double-buffered, global
 // loads running several chunks ahead through registers), so the vector unit
-// issues little besides v_fma.  Large batches give each wave 3 tokens x all
-// experts; small batches give each wave 1 token x 64 experts, the shortest
-// dependent chain, with a deeper prefetch.  Larger E uses the generic kernel.  Selection happens in registers with wave-wide
-// 64-bit max reductions over (orderable logit, ~expert) keys.
+// issues little besides v_fma.  Large bf16 batches with scratch screen the
+// experts with MFMA estimates and run the chains of the candidates only; other
+// large batches give each wave 3 tokens x all experts; small batches with
+// scratch give each one-wave workgroup a tile of 8 tokens x 8 experts (the
+// chain length sets their time), without scratch each wave 1 token x 64
+// experts.  Larger E uses the generic kernel.  Selection happens in registers
+// with wave-wide 64-bit max reductions over (orderable logit, ~expert) keys.
 #include "common.hpp"
 #include "route_prefetch.hpp"
 
@@ -347,21 +350,19 @@ __global__ __launch_bounds__(WAVES * 64) void route_fast_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Small batches, E <= 128: one chain per lane, one workgroup per TPW tokens,
-// so that a batch of a hundred tokens still spreads over a hundred CUs and the
-// run time approaches the length of one dependent fma chain.
+// Small batches without scratch for the logits, E <= 128: one chain per lane,
+// one workgroup per TPW tokens, so that a batch of a hundred tokens still
+// spreads over a hundred CUs.  (With scratch, or logits requested, the tiled
+// kernel below streams far less and is used instead.)
 //
 // A workgroup has CW = TPW * WE chain waves (token ti, experts g*64 + lane)
 // and DW copy waves.  The copy waves stream the router weight through an
 // NB-deep ring of HC-row chunks straight into LDS (16-byte DMA; rows padded to
-// EP = 64 * WE elements), so the chain waves spend their issue slots on little
-// besides v_fmac and LDS reads.  The token rows are widened to float32 in LDS
-// once.  Per group of 8 rows a chain wave waits for that group's operands and
-// then alternates its 8 dependent fmas with the 10 reads of the group two
-// ahead (4 register slots): between two dependent fmas the wave has an issue
-// slot to spare, which the reads fill.  A bf16 weight is read into the high
-// half of a register whose low half is zero from the start, which is exactly
-// its float32 value.
+// EP = 64 * WE elements).  The token rows are widened to float32 in LDS once.
+// A chain wave keeps four register slots of operands (8 rows each): while it
+// runs the 8 dependent fmas of one group it reads the group two ahead, the
+// compiler placing the waits and a scheduling pattern interleaving the reads
+// with the fmas.  A bf16 weight widens exactly to float32 by a 16-bit shift.
 // ---------------------------------------------------------------------------
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
@@ -372,78 +373,30 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// The group's own operands (x0, x1, w) are used after at most N younger LDS
-// reads remain outstanding (reads return in order); the next operands (nx0,
-// nx1, nw) are written when their reads land, two groups later.
-#define MOE_CHAIN_GROUP(RD)                                                                                     \
-    asm volatile("s_waitcnt lgkmcnt(%[n])\n\t"                                                                \
-                 "v_fmac_f32 %[acc], %[a0], %[w0]\n\t"                                                        \
-                 "ds_read_b128 %[nx0], %[ax] offset:%[ox0]\n\t"                                               \
-                 "v_fmac_f32 %[acc], %[a1], %[w1]\n\t"                                                        \
-                 "ds_read_b128 %[nx1], %[ax] offset:%[ox1]\n\t"                                               \
-                 "v_fmac_f32 %[acc], %[a2], %[w2]\n\t"                                                        \
-                 RD " %[n0], %[aw] offset:%[o0]\n\t"                                                          \
-                 "v_fmac_f32 %[acc], %[a3], %[w3]\n\t"                                                        \
-                 RD " %[n1], %[aw] offset:%[o1]"                                                              \
-                 : [acc] "+v"(acc), [nx0] "=&v"(nx0), [nx1] "=&v"(nx1), [n0] "+v"(nw[0]), [n1] "+v"(nw[1])    \
-                 : [a0] "v"(x0[0]), [a1] "v"(x0[1]), [a2] "v"(x0[2]), [a3] "v"(x0[3]), [w0] "v"(w[0]),       \
-                   [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [ax] "v"(ax), [aw] "v"(aw), [n] "i"(N),   \
-                   [ox0] "i"(OX), [ox1] "i"(OX + 16), [o0] "i"(OW), [o1] "i"(OW + RB));                        \
-    asm volatile("v_fmac_f32 %[acc], %[a4], %[w4]\n\t"                                                        \
-                 RD " %[n2], %[aw] offset:%[o2]\n\t"                                                          \
-                 "v_fmac_f32 %[acc], %[a5], %[w5]\n\t"                                                        \
-                 RD " %[n3], %[aw] offset:%[o3]\n\t"                                                          \
-                 "v_fmac_f32 %[acc], %[a6], %[w6]\n\t"                                                        \
-                 RD " %[n4], %[aw] offset:%[o4]\n\t"                                                          \
-                 "v_fmac_f32 %[acc], %[a7], %[w7]\n\t"                                                        \
-                 RD " %[n5], %[aw] offset:%[o5]\n\t"                                                          \
-                 RD " %[n6], %[aw] offset:%[o6]\n\t"                                                          \
-                 RD " %[n7], %[aw] offset:%[o7]"                                                              \
-                 : [acc] "+v"(acc), [n2] "+v"(nw[2]), [n3] "+v"(nw[3]), [n4] "+v"(nw[4]), [n5] "+v"(nw[5]),  \
-                   [n6] "+v"(nw[6]), [n7] "+v"(nw[7])                                                         \
-                 : [a4] "v"(x1[0]), [a5] "v"(x1[1]), [a6] "v"(x1[2]), [a7] "v"(x1[3]), [w4] "v"(w[4]),       \
-                   [w5] "v"(w[5]), [w6] "v"(w[6]), [w7] "v"(w[7]), [aw] "v"(aw), [o2] "i"(OW + 2 * RB),      \
-                   [o3] "i"(OW + 3 * RB), [o4] "i"(OW + 4 * RB), [o5] "i"(OW + 5 * RB), [o6] "i"(OW + 6 * RB), \
-                   [o7] "i"(OW + 7 * RB))
-
-template <bool BF16, int N, int RB, int OX, int OW>
-__device__ __forceinline__ void chain_group(float& acc, const floatx4& x0, const floatx4& x1, const float (&w)[8],
-                                            floatx4& nx0, floatx4& nx1, float (&nw)[8], uint32_t ax, uint32_t aw) {
-    if constexpr (BF16) {
-        MOE_CHAIN_GROUP("ds_read_u16_d16_hi");
-    } else {
-        MOE_CHAIN_GROUP("ds_read_b32");
+// Operands of one group of 8 rows: the token row's 8 values (two 16-byte
+// reads) and the chain's 8 weights (one column of the staged rows).  A bf16
+// weight widens exactly to float32 by a 16-bit shift.
+template <typename XT>
+__device__ __forceinline__ void chain_fetch(floatx4& x0, floatx4& x1, float (&w)[8], const float* __restrict__ sx,
+                                            const XT* __restrict__ sw, int rb) {
+    x0 = *reinterpret_cast<const floatx4*>(sx);
+    x1 = *reinterpret_cast<const floatx4*>(sx + 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if constexpr (sizeof(XT) == 2)
+            w[j] = __uint_as_float(static_cast<uint32_t>(sw[j * rb]) << 16);
+        else
+            w[j] = sw[j * rb];
     }
 }
-#undef MOE_CHAIN_GROUP
 
-// The reads of one group with no fmas (the first two groups of the chain).
-#define MOE_CHAIN_FETCH(RD)                                                                                     \
-    asm volatile("ds_read_b128 %[nx0], %[ax] offset:%[ox0]\n\t"                                               \
-                 "ds_read_b128 %[nx1], %[ax] offset:%[ox1]\n\t"                                               \
-                 RD " %[n0], %[aw] offset:%[o0]\n\t"                                                          \
-                 RD " %[n1], %[aw] offset:%[o1]\n\t"                                                          \
-                 RD " %[n2], %[aw] offset:%[o2]\n\t"                                                          \
-                 RD " %[n3], %[aw] offset:%[o3]\n\t"                                                          \
-                 RD " %[n4], %[aw] offset:%[o4]\n\t"                                                          \
-                 RD " %[n5], %[aw] offset:%[o5]\n\t"                                                          \
-                 RD " %[n6], %[aw] offset:%[o6]\n\t"                                                          \
-                 RD " %[n7], %[aw] offset:%[o7]"                                                              \
-                 : [nx0] "=&v"(nx0), [nx1] "=&v"(nx1), [n0] "+v"(nw[0]), [n1] "+v"(nw[1]), [n2] "+v"(nw[2]),  \
-                   [n3] "+v"(nw[3]), [n4] "+v"(nw[4]), [n5] "+v"(nw[5]), [n6] "+v"(nw[6]), [n7] "+v"(nw[7])   \
-                 : [ax] "v"(ax), [aw] "v"(aw), [ox0] "i"(OX), [ox1] "i"(OX + 16), [o0] "i"(OW),               \
-                   [o1] "i"(OW + RB), [o2] "i"(OW + 2 * RB), [o3] "i"(OW + 3 * RB), [o4] "i"(OW + 4 * RB),    \
-                   [o5] "i"(OW + 5 * RB), [o6] "i"(OW + 6 * RB), [o7] "i"(OW + 7 * RB))
-
-template <bool BF16, int RB, int OX, int OW>
-__device__ __forceinline__ void chain_fetch(floatx4& nx0, floatx4& nx1, float (&nw)[8], uint32_t ax, uint32_t aw) {
-    if constexpr (BF16) {
-        MOE_CHAIN_FETCH("ds_read_u16_d16_hi");
-    } else {
-        MOE_CHAIN_FETCH("ds_read_b32");
-    }
+// The group's 8 dependent steps, rows in ascending order.
+__device__ __forceinline__ void chain_steps(float& acc, const floatx4& x0, const floatx4& x1, const float (&w)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(x0[j], w[j], acc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(x1[j], w[4 + j], acc);
 }
-#undef MOE_CHAIN_FETCH
 
 // Reads units [b*n/B, (b+1)*n/B) of a region of n 1 KiB units (workgroup b of
 // B) into a scratch KiB of LDS per wave, up to 32 copies in flight per wave,
@@ -575,36 +528,39 @@ __global__ __launch_bounds__((TPW * WE + DW) * 64) void route_chain_kernel(
         }
         wait_lgkmcnt0();                       // the staged rows are written before the barrier
 
+        // Four register slots: group Q computes from slot Q % 4 while the reads of
+        // group Q + 2 fill slot (Q + 2) % 4; the compiler places the waits for
+        // them, and a scheduling pattern interleaves the reads with the
+        // dependent fmas (each fma leaves an issue slot that a read can fill).
         floatx4 xv[4][2];
         float wv[4][8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) wv[k][j] = 0.0f;   // low halves stay zero (bf16 reads fill the high half)
-        auto lds = [](const void* p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)); };
-        const uint32_t ax0 = lds(s_x[ti]);
-        const uint32_t aw0 = lds(&s_w[0][ec]);
-        constexpr uint32_t kStage = HC * EP * sizeof(XT);
+        const float* sx0 = s_x[ti];
+        const XT* sw0 = &s_w[0][ec];
 
         __builtin_amdgcn_s_barrier();          // chunk 0 and the token rows are in LDS
-        chain_fetch<BF16, RB, 0, 0>(xv[0][0], xv[0][1], wv[0], ax0, aw0);
-        chain_fetch<BF16, RB, 32, 8 * RB>(xv[1][0], xv[1][1], wv[1], ax0, aw0);
+        chain_fetch<XT>(xv[0][0], xv[0][1], wv[0], sx0, sw0, EP);
+        chain_fetch<XT>(xv[1][0], xv[1][1], wv[1], sx0 + 8, sw0 + 8 * EP, EP);
         for (int c = 0; c < nc; ++c) {
             __builtin_amdgcn_s_barrier();      // chunk c+1 is in LDS; stage c-1 may be refilled
-            const uint32_t axc = ax0 + c * HC * 4;
-            const uint32_t axn = ax0 + min(c + 1, nc - 1) * HC * 4;
-            const uint32_t awc = aw0 + (c % NB) * kStage;
-            const uint32_t awn = aw0 + ((c + 1) % NB) * kStage;
+            const float* sxc = sx0 + c * HC;
+            const float* sxn = sx0 + min(c + 1, nc - 1) * HC;
+            const XT* swc = sw0 + (c % NB) * (HC * EP);
+            const XT* swn = sw0 + ((c + 1) % NB) * (HC * EP);
             static_for<GPC>([&](auto qc) {
                 constexpr int Q = decltype(qc)::value;
                 constexpr int S = Q % 4, NS = (Q + 2) % 4, QN = (Q + 2) % GPC;
                 constexpr bool NEXT = Q + 2 >= GPC;
-                chain_group<BF16, 10, RB, QN * 32, QN * 8 * RB>(acc, xv[S][0], xv[S][1], wv[S], xv[NS][0],
-                                                                xv[NS][1], wv[NS], NEXT ? axn : axc,
-                                                                NEXT ? awn : awc);
+                chain_fetch<XT>(xv[NS][0], xv[NS][1], wv[NS], (NEXT ? sxn : sxc) + QN * 8,
+                                (NEXT ? swn : swc) + QN * 8 * EP, EP);
+                chain_steps(acc, xv[S][0], xv[S][1], wv[S]);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // the two token-row reads
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one fma (or widening) ...
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // ... one weight read
+                }
             });
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the look-ahead reads past the end
     }
 
     if (wave < CW) {
@@ -634,6 +590,130 @@ __global__ __launch_bounds__((TPW * WE + DW) * 64) void route_chain_kernel(
                 select_and_write<2>(l, E, K, t, topk_idx, topk_w);
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small batches with somewhere to put the logits: a workgroup computes a tile
+// of TT tokens x TE experts, one chain per lane (token tid / TE, expert
+// tid % TE), so it streams TT token rows and TE weight columns instead of the
+// whole router weight per token.  The threads hold the next chunks' operands
+// in a ring of RD HC-row chunks in registers (global loads issued RD - 1
+// chunks ahead) while the chains run over the current chunk, then widen the
+// next one to float32 into the other LDS buffer: token rows [TT][HC] and the weight columns transposed to
+// [TE][HC], rows padded by 4 floats so that the 16 weight rows one read
+// touches fall on distinct banks.  A lane reads 4 h of its token and of its
+// expert with two 16-byte reads and runs 4 dependent fmas; the compiler places
+// every wait.  A selection pass over the written logits picks the top K.
+// Workgroups past the tiles warm the last-level cache like the chain kernel's.
+// ---------------------------------------------------------------------------
+template <typename XT, int TT, int TE, int HC, int RD>
+__global__ __launch_bounds__(TT * TE) void route_tile_kernel(
+    const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias, int T, int H, int E,
+    float* __restrict__ logits, int ntile, const uint16_t* __restrict__ pf, int64_t pf_units) {
+    constexpr int NT = TT * TE;                      // threads, one chain each
+    constexpr int VEC = 16 / static_cast<int>(sizeof(XT));
+    constexpr int HP = HC + 4;                       // padded LDS row (floats)
+    constexpr int XPR = HC / VEC;                    // 16-byte pieces per token row of a chunk
+    constexpr int WPR = TE / VEC;                    // 16-byte pieces per weight row of a tile
+    constexpr int XL = TT * XPR / NT;                // token pieces per thread and chunk
+    constexpr int WL = HC * WPR / NT;                // weight pieces per thread and chunk
+    static_assert(XL >= 1 && WL >= 1 && TT * XPR % NT == 0 && HC * WPR % NT == 0, "chunk split");
+    static_assert(TE % VEC == 0 && HC % 4 == 0, "pieces");
+    __shared__ __attribute__((aligned(16))) float s_x[2][TT][HP];
+    __shared__ __attribute__((aligned(16))) float s_w[2][TE][HP];
+    if (static_cast<int>(blockIdx.x) >= ntile) {
+        cache_region(pf, pf_units, blockIdx.x - ntile, gridDim.x - ntile, &s_x[0][0][0]);
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int net = (E + TE - 1) / TE;
+    const int tok0 = (static_cast<int>(blockIdx.x) / net) * TT;
+    const int e0 = (static_cast<int>(blockIdx.x) % net) * TE;
+    const int nc = H / HC;
+
+    // a ring of RD chunks in registers: chunk c sits in slot c % RD, loaded RD - 1 chunks ahead
+    u32x4 xr[RD][XL], wr[RD][WL];
+    // token rows past T repeat row T-1; weight pieces past E repeat the last piece (both unused)
+    auto load = [&](int c, int q) {
+        const int h0 = c * HC;
+#pragma unroll
+        for (int j = 0; j < XL; ++j) {
+            const int i = j * NT + tid;
+            const int t = min(tok0 + i / XPR, T - 1);
+            xr[q][j] = *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t) * H + h0 + (i % XPR) * VEC);
+        }
+#pragma unroll
+        for (int j = 0; j < WL; ++j) {
+            const int i = j * NT + tid;
+            const int ec = min(e0 + (i % WPR) * VEC, E - VEC);
+            wr[q][j] = *reinterpret_cast<const u32x4*>(w + static_cast<int64_t>(h0 + i / WPR) * E + ec);
+        }
+    };
+    auto widen = [](const u32x4& r, int v) -> float {
+        if constexpr (sizeof(XT) == 2) {
+            const uint32_t u = r[v >> 1];
+            return __uint_as_float((v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+        } else {
+            return __uint_as_float(r[v]);
+        }
+    };
+    auto store = [&](int b, int q) {
+#pragma unroll
+        for (int j = 0; j < XL; ++j) {
+            const int i = j * NT + tid;
+            float* dst = &s_x[b][i / XPR][(i % XPR) * VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; v += 4)
+                *reinterpret_cast<floatx4*>(dst + v) = floatx4{widen(xr[q][j], v), widen(xr[q][j], v + 1),
+                                                               widen(xr[q][j], v + 2), widen(xr[q][j], v + 3)};
+        }
+#pragma unroll
+        for (int j = 0; j < WL; ++j) {
+            const int i = j * NT + tid;
+            const int hr = i / WPR, g = i % WPR;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) s_w[b][g * VEC + v][hr] = widen(wr[q][j], v);
+        }
+    };
+
+    const int tl = tid / TE, el = tid % TE;
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < RD; ++q)
+        if (q < nc) load(q, q);
+    store(0, 0);
+    __syncthreads();
+    // chunk c: run the chains over LDS buffer c & 1, widen chunk c+1 into the other buffer (the one
+    // chunk c-1 used: everyone passed the last barrier), load chunk c+RD into the slot chunk c left
+    auto chunk = [&](int c, auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const int b = c & 1;
+        const float* px = s_x[b][tl];
+        const float* pw = s_w[b][el];
+#pragma unroll 8
+        for (int h = 0; h < HC; h += 4) {
+            const floatx4 xv = *reinterpret_cast<const floatx4*>(px + h);
+            const floatx4 wv = *reinterpret_cast<const floatx4*>(pw + h);
+            acc = __builtin_fmaf(xv[0], wv[0], acc);
+            acc = __builtin_fmaf(xv[1], wv[1], acc);
+            acc = __builtin_fmaf(xv[2], wv[2], acc);
+            acc = __builtin_fmaf(xv[3], wv[3], acc);
+        }
+        if (c + 1 < nc) store(b ^ 1, (q + 1) % RD);
+        if (c + RD < nc) load(c + RD, q);
+        __syncthreads();
+    };
+    for (int c0 = 0; c0 < nc; c0 += RD) {
+        static_for<RD>([&](auto qc) {
+            if (c0 + decltype(qc)::value < nc) chunk(c0 + decltype(qc)::value, qc);
+        });
+    }
+    const int t = tok0 + tl, e = e0 + el;
+    if (t < T && e < E) {
+        float v = acc;
+        if (bias != nullptr) v = v + bias[e];
+        logits[static_cast<int64_t>(t) * E + e] = v;
     }
 }
 
@@ -671,23 +751,48 @@ void launch_fast(const moe_shape& s, const XT* x, const XT* w, const float* bias
                        w, bias, s.T, s.H, s.E, s.K, idx, tw, logits);
 }
 
+// spare CUs past `grid` routing workgroups, to warm the last-level cache with pf
+int prefetch_workgroups(int grid, const CachePrefetch& pf) {
+    if (pf.region == nullptr || pf.bytes < 1024) return 0;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return grid < cus ? cus - grid : 0;
+}
+
 template <typename XT, int TPW, int WE, int DW, int HC, int NB, int XMAX>
 void launch_chain(const moe_shape& s, const XT* x, const XT* w, const float* bias, int32_t* idx, float* tw,
                   float* logits, const CachePrefetch& pf, hipStream_t st) {
     const int grid = (s.T + TPW - 1) / TPW;
     // spare CUs read the prefetch region while the routing workgroups run
-    int extra = 0;
-    if (pf.region != nullptr && pf.bytes >= 1024) {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            int v = 0;
-            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-        }
-        if (grid < cus) extra = cus - grid;
-    }
+    const int extra = prefetch_workgroups(grid, pf);
     hipLaunchKernelGGL((route_chain_kernel<XT, TPW, WE, DW, HC, NB, XMAX>), dim3(grid + extra),
                        dim3((TPW * WE + DW) * 64), 0, st, x, w, bias, s.T, s.H, s.E, s.K, idx, tw, logits, grid,
                        static_cast<const uint16_t*>(pf.region), static_cast<int64_t>(pf.bytes / 1024));
+}
+
+constexpr int kTileTokens = 8;      // tiled router: tokens x experts per workgroup (one wave), h per chunk
+constexpr int kTileExperts = 8;
+constexpr int kTileChunk = 256;
+constexpr int kTileRing = 2;        // chunks in flight through registers
+constexpr int kTileMaxT = 1024;
+
+bool tile_eligible(const moe_shape& s, int x_dtype) {
+    const int vec = x_dtype == MOE_BF16 ? 8 : 4;
+    return s.T <= kTileMaxT && s.E % vec == 0 && s.H % kTileChunk == 0;
+}
+
+template <typename XT>
+void launch_tile(const moe_shape& s, const XT* x, const XT* w, const float* bias, float* logits, int32_t* idx,
+                 float* tw, const CachePrefetch& pf, hipStream_t st) {
+    const int ntile = ((s.T + kTileTokens - 1) / kTileTokens) * ((s.E + kTileExperts - 1) / kTileExperts);
+    const int extra = prefetch_workgroups(ntile, pf);
+    hipLaunchKernelGGL((route_tile_kernel<XT, kTileTokens, kTileExperts, kTileChunk, kTileRing>), dim3(ntile + extra),
+                       dim3(kTileTokens * kTileExperts), 0, st, x, w, bias, s.T, s.H, s.E, logits, ntile,
+                       static_cast<const uint16_t*>(pf.region), static_cast<int64_t>(pf.bytes / 1024));
+    launch_route_from_logits(s, logits, idx, tw, st);
 }
 
 template <typename XT>
@@ -1432,6 +1537,13 @@ size_t route_screen_bytes(const moe_shape& s, int x_dtype, int w_dtype) {
     return screen_eligible(s, x_dtype, w_dtype) ? screen_layout(s, nullptr).bytes : 0;
 }
 
+size_t route_workspace_bytes(const moe_shape& s) {
+    // the screened path (bf16 only) or the tiled path's logits (float32 eligibility includes bf16's)
+    const size_t screen = route_screen_bytes(s, MOE_BF16, MOE_BF16);
+    const size_t tile = tile_eligible(s, MOE_F32) ? static_cast<size_t>(s.T) * s.E * sizeof(float) : 0;
+    return screen > tile ? screen : tile;
+}
+
 bool route_screen_layout(const moe_shape& s, int x_dtype, int w_dtype, moe_route_screen_info* info) {
     if (!screen_eligible(s, x_dtype, w_dtype)) return false;
     const ScreenWs w = screen_layout(s, nullptr);
@@ -1453,10 +1565,20 @@ int launch_route_prefetch(const moe_shape& s, const void* x, int x_dtype, const 
                           int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
                           hipStream_t st, CachePrefetch pf) {
     const size_t need = route_screen_bytes(s, x_dtype, x_dtype);
-    if (logits == nullptr && ws != nullptr && need > 0 && ws_bytes >= need)
+    const size_t tile_need = static_cast<size_t>(s.T) * s.E * sizeof(float);
+    if (logits == nullptr && ws != nullptr && need > 0 && ws_bytes >= need) {
         launch_route_screened(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias, topk_idx,
                               topk_w, ws, st);
-    else if (x_dtype == MOE_BF16)
+    } else if (tile_eligible(s, x_dtype) && (logits != nullptr || (ws != nullptr && ws_bytes >= tile_need))) {
+        // the logits go to the caller's array, else to the workspace
+        float* l = logits != nullptr ? logits : static_cast<float*>(ws);
+        if (x_dtype == MOE_BF16)
+            launch_tile<uint16_t>(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias, l,
+                                  topk_idx, topk_w, pf, st);
+        else
+            launch_tile<float>(s, static_cast<const float*>(x), static_cast<const float*>(w), bias, l, topk_idx,
+                               topk_w, pf, st);
+    } else if (x_dtype == MOE_BF16)
         launch_route_dt<uint16_t>(s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
                                   topk_idx, topk_w, logits, pf, st);
     else

@@ -89,7 +89,7 @@ def test_invalid_pointers_and_enums():
              None) == B.MOE_ERR_WORKSPACE
     assert R(S128, p16, B.MOE_BF16, p16, B.MOE_BF16, None, p16, p16, None, odd, rneed,
              None) == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_route_workspace_bytes(S) == 0            # 8 experts: no screened path
+    assert lib.moe_route_workspace_bytes(S) == 64 * 8 * 4   # 8 experts: no screened path; the tiled path's logits
     s192 = _shape(T=1000, E=128, K=8, e_end=32, H=192).c()
     assert lib.moe_route_workspace_bytes(ctypes.byref(s192)) == 0   # H not a multiple of 128
     assert lib.moe_layer_workspace_bytes(S128) >= rneed

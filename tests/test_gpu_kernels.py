@@ -49,14 +49,26 @@ def test_route_bit_exact_bf16(B, T, H, E, K):
 
 @pytest.mark.parametrize("T,H,E,K,dt", [(1, 4096, 128, 8, "bf16"), (128, 4096, 128, 8, "bf16"),
                                         (1024, 256, 128, 8, "bf16"), (7, 128, 72, 4, "bf16"),
-                                        (33, 64, 24, 2, "f32"), (100, 320, 64, 64, "f32"), (50, 4096, 16, 16, "f32"),
-                                        (65, 192, 120, 8, "f32")])
+                                        (5, 128, 8, 2, "bf16"), (33, 64, 24, 2, "f32"), (100, 320, 64, 64, "f32"),
+                                        (50, 4096, 16, 16, "f32"), (65, 192, 120, 8, "f32"), (17, 256, 20, 4, "f32")])
 def test_route_small_batch_bit_exact(B, T, H, E, K, dt):
-    """Batches of at most 1024 tokens: one workgroup per token, rows staged with padding past E."""
+    """Batches of at most 1024 tokens, both small-batch forms: with somewhere
+    to put the logits (H a multiple of 128) the tiled form (16 tokens x 16
+    experts per workgroup, tiles cut by T and E); without (no workspace, no
+    logits output) one workgroup per token.  Logits bit-exact, selections equal."""
     idx, tw, lg, ri, rw, rl = _route_case(B, T, H, E, K, dtype=dt, seed=T + E)
     assert np.array_equal(lg.view(np.uint32), rl.view(np.uint32)), "logits differ from the fixed fma order"
     assert np.array_equal(idx, ri)
     assert np.abs(tw - rw).max() <= 1e-6
+    rng = np.random.default_rng(T + E)
+    x = rng.standard_normal((T, H), dtype=np.float32)
+    w = rng.standard_normal((H, E), dtype=np.float32) * np.float32(0.02)
+    if dt == "bf16":
+        x, w = _bf16(x), _bf16(w)
+    idx_c, tw_c, _ = B.moe_route(B.Shape(T, H, E, K, 64, 0, E), to_torch(x), to_torch(w), screened=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_c.cpu().numpy(), ri), "per-token form"
+    assert np.array_equal(tw_c.cpu().numpy(), tw), "per-token form"
 
 
 def test_route_bit_exact_f32_tiny(B):
@@ -142,9 +154,10 @@ def test_route_screened_bias_ties_and_degenerate(B):
     # zero router: no estimate error, every expert a candidate; experts 0..K-1, weights 1/K
     idx, tw, _, _ = _screened(B, x[:577, :128].copy(), np.zeros((128, 128), np.uint16), 8)
     assert np.array_equal(idx, np.tile(np.arange(8), (577, 1))) and np.all(tw == np.float32(0.125))
-    # H not a multiple of 128, or fewer than 512 tokens: no screened path (no workspace)
+    # H not a multiple of 128: no screened path and no tiled one (no workspace); fewer than 512
+    # tokens: no screened path, the workspace holds the tiled path's logits
     assert B.moe_route_workspace_bytes(B.Shape(600, 192, 128, 8, 64, 0, 128)) == 0
-    assert B.moe_route_workspace_bytes(B.Shape(511, 256, 128, 8, 64, 0, 128)) == 0
+    assert B.moe_route_workspace_bytes(B.Shape(511, 256, 128, 8, 64, 0, 128)) == 511 * 128 * 4
     idx, tw, lg = B.moe_route(B.Shape(600, 192, 128, 8, 64, 0, 128), to_torch(x[:600, :192].copy()),
                               to_torch(w[:192].copy()))
     torch.cuda.synchronize()
