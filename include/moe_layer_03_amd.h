@@ -80,10 +80,14 @@ typedef struct moe_shape {
 size_t moe_dispatch_workspace_bytes(const moe_shape* s);
 
 /*
- * Bytes of scratch memory that let moe_route() take its screened path
- * (host-only, no HIP call): bf16 inputs, E == 128, T >= 512, H a multiple
- * of 128 and at most 65536, no logits output.  0 when the shape cannot take
- * it.
+ * Bytes of scratch memory that let moe_route() take its faster paths
+ * (host-only, no HIP call), the larger of:
+ *   the screened path: bf16 inputs, E == 128, T >= 512, H a multiple of 128
+ *     and at most 65536, no logits output;
+ *   the tiled small-batch path: T <= 1024, E a multiple of 8 (bf16) or 4
+ *     (float32), H a multiple of 256: T * E * 4 bytes of logits (not needed
+ *     when the caller asks for logits).
+ * 0 when the shape takes neither.
  */
 size_t moe_route_workspace_bytes(const moe_shape* s);
 
@@ -153,11 +157,11 @@ int moe_pack_weights(const moe_shape* s, const void* w_gate, const void* w_up, c
  *       over the chosen K, i.e. the softmax probabilities renormalised.
  *   ws, ws_bytes: scratch memory, or NULL.  With ws != NULL (16-byte aligned,
  *       ws_bytes >= moe_route_workspace_bytes(s), else MOE_ERR_WORKSPACE) and
- *       a shape that allows it, logits are first estimated with bf16 MFMA and
+ *       a large bf16 batch, logits are first estimated with bf16 MFMA and
  *       only the experts a rigorous error bound cannot exclude from the top K
- *       are evaluated in the fma chain above; the outputs are identical to
- *       evaluating every logit, which is what happens with ws == NULL or
- *       when logits are requested.
+ *       are evaluated in the fma chain above; a small batch writes its logits
+ *       to ws (or to logits) and selects from them.  The outputs are
+ *       identical on every path, which is what happens with ws == NULL.
  */
 int moe_route(const moe_shape* s, const void* x, int x_dtype, const void* w_router, int w_dtype,
               const float* bias, int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,

@@ -50,10 +50,11 @@ def test_route_bit_exact_bf16(B, T, H, E, K):
 @pytest.mark.parametrize("T,H,E,K,dt", [(1, 4096, 128, 8, "bf16"), (128, 4096, 128, 8, "bf16"),
                                         (1024, 256, 128, 8, "bf16"), (7, 128, 72, 4, "bf16"),
                                         (5, 128, 8, 2, "bf16"), (33, 64, 24, 2, "f32"), (100, 320, 64, 64, "f32"),
-                                        (50, 4096, 16, 16, "f32"), (65, 192, 120, 8, "f32"), (17, 256, 20, 4, "f32")])
+                                        (50, 4096, 16, 16, "f32"), (65, 192, 120, 8, "f32"), (17, 256, 20, 4, "f32"),
+                                        (9, 512, 24, 4, "bf16")])
 def test_route_small_batch_bit_exact(B, T, H, E, K, dt):
     """Batches of at most 1024 tokens, both small-batch forms: with somewhere
-    to put the logits (H a multiple of 128) the tiled form (16 tokens x 16
+    to put the logits (H a multiple of 256) the tiled form (8 tokens x 8
     experts per workgroup, tiles cut by T and E); without (no workspace, no
     logits output) one workgroup per token.  Logits bit-exact, selections equal."""
     idx, tw, lg, ri, rw, rl = _route_case(B, T, H, E, K, dtype=dt, seed=T + E)
