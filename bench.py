@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA and copy rate probes")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens in the oracle's timed sample")
+    ap.add_argument("--mxfp8-only", action="store_true",
+                    help="measure the workload's MXFP8 path only and print its result object (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the timed region, run a plain device copy (torch.neg) of this many MiB twice, "
                          "so a counter run can scale FETCH_SIZE/WRITE_SIZE against a kernel of known traffic")
@@ -117,6 +119,19 @@ def measure_peaks(torch, B, dev):
     del src, dst
     torch.cuda.empty_cache()
     return res
+
+
+def copy_probe(torch, dev, mib):
+    """A plain device copy (torch.neg over `mib` MiB of float32, twice): a counter run scales FETCH_SIZE and
+    WRITE_SIZE by what they read for this kernel of known traffic."""
+    if mib <= 0:
+        return
+    src = torch.randn(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def measure(wl, steps, warmup, graph, copy_probe_mib=0):
@@ -196,14 +211,7 @@ def measure(wl, steps, warmup, graph, copy_probe_mib=0):
         if ev is not None:
             ev[5].record()
 
-    if copy_probe_mib > 0:
-        n = copy_probe_mib * (1 << 20) // 4
-        src = torch.randn(n, dtype=f32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_probe(torch, dev, copy_probe_mib)
 
     # the fused entry point, on buffers of its own (moe_layer carves its scratch from one workspace)
     ws_layer = torch.empty(max(B.moe_layer_workspace_bytes(s), 16), dtype=torch.uint8, device=dev)
@@ -317,7 +325,7 @@ def measure(wl, steps, warmup, graph, copy_probe_mib=0):
     return res, inp
 
 
-def measure_mxfp8(wl, steps, warmup):
+def measure_mxfp8(wl, steps, warmup, copy_probe_mib=0):
     """The layer share with MXFP8 expert GEMMs (moe_layer_mxfp8): fused steps with a HIP event per step, then
     the staged calls with events around route, activation quantisation, dispatch, gate/up, down and combine."""
     import numpy as np
@@ -356,6 +364,7 @@ def measure_mxfp8(wl, steps, warmup):
              ws_d=torch.empty(max(B.moe_dispatch_workspace_bytes(s), 16), dtype=torch.uint8, device=dev))
     stages = ["route", "quantize_x", "dispatch", "gemm_gate_up", "gemm_down", "combine"]
     dd = {}
+    copy_probe(torch, dev, copy_probe_mib)
 
     def staged(ev=None):
         def mark(i):
@@ -409,15 +418,19 @@ def measure_mxfp8(wl, steps, warmup):
     gu_flops = n_loc * 2 * H * 2 * I
     gu_bytes = active * 2 * H * I * (1 + 1 / 32) + n_loc * H * (1 + 1 / 32) + n_loc * I * (1 + 1 / 32)
     t_gu = stage_ms["gemm_gate_up"] * 1e-3
-    if gu_flops / gu_bytes >= PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+    # the launcher's rule: few rows per expert stream the weights (HBM-bound form), else the tiled MFMA form
+    # (at the prefill shard the gate/up problem sits at the fp8 ridge, so intensity alone cannot name it)
+    if T * wl.K > 64 * E:
         ach = gu_flops / t_gu / 1e12
         roof = dict(kernel="grouped_gemm_mx_kernel (gate/up, scaled fp8 MFMA)", bound="mfma", achieved=round(ach, 2),
                     peak=PEAK_FP8_TFLOPS, unit="TFLOP/s", frac=round(ach / PEAK_FP8_TFLOPS, 4),
+                    traffic=measured_traffic(wl.name, "mxfp8"),
                     per_launch=dict(flops=gu_flops, us=round(t_gu * 1e6, 2)))
     else:
         ach = gu_bytes / t_gu / 1e9
         roof = dict(kernel="grouped_gemm_mx_skinny_kernel (gate/up, scaled fp8 MFMA)", bound="hbm",
                     achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4),
+                    traffic=measured_traffic(wl.name, "mxfp8"),
                     per_launch=dict(bytes=int(gu_bytes), us=round(t_gu * 1e6, 2)))
     sec = ms * 1e-3
     res = {"workload": wl.name, "steps": steps, "ms_per_step": round(ms, 4),
@@ -508,6 +521,10 @@ def main():
     B.load()
 
     wl = W.WORKLOADS[args.workload]
+    if args.mxfp8_only:
+        print(json.dumps({"workload": wl.name, "mxfp8": measure_mxfp8(wl, args.steps, args.warmup,
+                                                                     args.copy_probe_mib)}), flush=True)
+        return
     head, inp = measure(wl, args.steps, args.warmup, args.graph, args.copy_probe_mib)
     print(f"[bench] {wl.name}: {head['ms_per_step']} ms/step", file=sys.stderr, flush=True)
 
@@ -586,7 +603,12 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def measured_traffic(workload):
+# sources of each gate/up GEMM form, hashed into its counter summary
+TRAFFIC_SOURCES = {"bf16": ("gemm.hip", "gemm_common.hpp", "common.hpp"),
+                   "mxfp8": ("mxfp8.hip", "gemm_common.hpp", "common.hpp")}
+
+
+def measured_traffic(workload, kind="bf16"):
     """HBM bytes per gate/up GEMM launch from the committed counter summary of this workload, or None.
 
     The summary's ``traffic:`` line holds FETCH_SIZE/WRITE_SIZE scaled by a plain copy of known size, and a
@@ -594,7 +616,8 @@ def measured_traffic(workload):
     """
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    name = f"kernels_{workload}.md" if kind == "bf16" else f"kernels_mxfp8_{workload}.md"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     m = re.search(r"^traffic: kernel=gate_up read_bytes=(\d+) write_bytes=(\d+) sources_sha256=([0-9a-f]+)$",
@@ -602,7 +625,7 @@ def measured_traffic(workload):
     if not m:
         return None
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.hpp"):
+    for f in TRAFFIC_SOURCES[kind]:
         with open(os.path.join(ROOT, "moe_layer_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if h.hexdigest() != m.group(3):
