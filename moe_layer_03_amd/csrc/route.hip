@@ -60,53 +60,70 @@ __device__ __forceinline__ int key_expert(uint64_t k) {
     return static_cast<int>(~static_cast<uint32_t>(k));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-        uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-        uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+// Largest value over the wave: a running maximum within each row of 16 lanes
+// by DPP row shifts (lanes shifted in from outside the row see 0, neutral for
+// an unsigned maximum), then the four row maxima read out to scalars.  No LDS
+// round trips.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+    return max(max(r0, r1), max(r2, r3));
 }
 
 // Select the top K of the wave's E logits (lane holds experts g*64 + lane) and
 // write indices and renormalised weights of token t.  Uniform control flow.
+// The order is that of make_key: larger logit first, then the smaller expert
+// index.  Each round takes the largest upper key half (the ordered logit bits)
+// over the experts still in play, then the lowest expert index holding it from
+// a ballot.  A retired expert's key half becomes 0, below every finite logit;
+// only a logit whose bits are all ones (a NaN) also maps to 0, so liveness is
+// consulted when the round's maximum is 0.  The weights are exp(l - l_max)
+// over their sum, added in rank order.
 template <int NE>
 __device__ __forceinline__ void select_and_write(const float (&l)[NE], int E, int K, int t,
                                                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
     const int lane = threadIdx.x & (kWave - 1);
-    uint64_t key[NE];
+    uint32_t kv[NE];
+    uint32_t dead = 0u;                              // bit g: expert g * 64 + lane is out of play
 #pragma unroll
     for (int g = 0; g < NE; ++g) {
-        const int e = g * kWave + lane;
-        key[g] = e < E ? make_key(l[g], e) : 0ull;
+        const bool in = g * kWave + lane < E;
+        kv[g] = in ? static_cast<uint32_t>(make_key(l[g], 0) >> 32) : 0u;
+        dead |= in ? 0u : (1u << g);
     }
     int my_e = 0;
-    float my_l = 0.0f;
+    uint32_t my_m = 0u;
     for (int k = 0; k < K; ++k) {
-        uint64_t best = 0ull;
+        uint32_t m = kv[0];
 #pragma unroll
-        for (int g = 0; g < NE; ++g) best = key[g] > best ? key[g] : best;
-        best = wave_max_u64(best);
+        for (int g = 1; g < NE; ++g) m = max(m, kv[g]);
+        m = wave_max_u32(m);
+        int best = -1;
+#pragma unroll
+        for (int g = 0; g < NE; ++g) {
+            const uint64_t b = __ballot(kv[g] == m && (m != 0u || ((dead >> g) & 1u) == 0u));
+            if (best < 0 && b != 0ull) best = g * kWave + __builtin_ctzll(b);
+        }
 #pragma unroll
         for (int g = 0; g < NE; ++g)
-            if (key[g] == best) key[g] = 0ull;
+            if (g * kWave + lane == best) {
+                kv[g] = 0u;
+                dead |= 1u << g;
+            }
         if (lane == k) {
-            my_e = key_expert(best);
-            my_l = key_logit(best);
+            my_e = best;
+            my_m = m;
         }
     }
-    const float l0 = __shfl(my_l, 0, kWave);
+    const float my_l = key_logit(static_cast<uint64_t>(my_m) << 32);
+    const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_l), 0));
     const float ex = lane < K ? expf(my_l - l0) : 0.0f;
-    const float sum = wave_sum(ex);
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), k));
     if (lane < K) {
         topk_idx[static_cast<int64_t>(t) * K + lane] = my_e;
         topk_w[static_cast<int64_t>(t) * K + lane] = ex / sum;
@@ -594,101 +611,130 @@ __global__ __launch_bounds__((TPW * WE + DW) * 64) void route_chain_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Small batches with somewhere to put the logits: a workgroup computes a tile
-// of TT tokens x TE experts, one chain per lane (token tid / TE, expert
-// tid % TE), so it streams TT token rows and TE weight columns instead of the
-// whole router weight per token.  The threads hold the next chunks' operands
-// in a ring of RD HC-row chunks in registers (global loads issued RD - 1
-// chunks ahead) while the chains run over the current chunk, then widen the
-// next one to float32 into the other LDS buffer: token rows [TT][HC] and the weight columns transposed to
-// [TE][HC], rows padded by 4 floats so that the 16 weight rows one read
-// touches fall on distinct banks.  A lane reads 4 h of its token and of its
-// expert with two 16-byte reads and runs 4 dependent fmas; the compiler places
-// every wait.  A selection pass over the written logits picks the top K.
+// Small batches with somewhere to put the logits.  A workgroup owns TT tokens
+// and CH * TE experts: CH chain waves, each a TT x TE tile with one chain per
+// lane (token lane / TE, expert lane % TE), and one copy wave.  The copy wave
+// streams the TT token rows and the CH * TE weight columns through a ring of
+// three LDS buffers of HC rows, widened to float32: token rows [TT][HC] and
+// the weight columns transposed to [CH * TE][HC], rows padded by 4 floats.
+// Its global loads run one chunk ahead in registers, and it fills chunk c + 2
+// while the chains run over chunk c, so one barrier per chunk orders both.
+// A chain step reads 4 h of its token and of its expert with two 16-byte
+// reads (each row is read by TE or TT lanes at once) and runs 4 dependent
+// fmas.  On one wave those reads and fmas serialise: the wave waits while an
+// LDS read returns its 1 KiB, so the copies and the widening are kept out of
+// the chain waves.  A selection pass over the written logits picks the top K.
 // Workgroups past the tiles warm the last-level cache like the chain kernel's.
 // ---------------------------------------------------------------------------
-template <typename XT, int TT, int TE, int HC, int RD>
-__global__ __launch_bounds__(TT * TE) void route_tile_kernel(
+template <typename XT, int TT, int TE, int CH, int HC>
+__global__ __launch_bounds__((CH + 1) * 64) void route_tile_kernel(
     const XT* __restrict__ x, const XT* __restrict__ w, const float* __restrict__ bias, int T, int H, int E,
     float* __restrict__ logits, int ntile, const uint16_t* __restrict__ pf, int64_t pf_units) {
-    constexpr int NT = TT * TE;                      // threads, one chain each
+    constexpr int NB = 3;                            // LDS ring: chains read c, copies fill c + 2
     constexpr int VEC = 16 / static_cast<int>(sizeof(XT));
     constexpr int HP = HC + 4;                       // padded LDS row (floats)
+    constexpr int EW = CH * TE;                      // weight columns per workgroup
     constexpr int XPR = HC / VEC;                    // 16-byte pieces per token row of a chunk
-    constexpr int WPR = TE / VEC;                    // 16-byte pieces per weight row of a tile
-    constexpr int XL = TT * XPR / NT;                // token pieces per thread and chunk
-    constexpr int WL = HC * WPR / NT;                // weight pieces per thread and chunk
-    static_assert(XL >= 1 && WL >= 1 && TT * XPR % NT == 0 && HC * WPR % NT == 0, "chunk split");
-    static_assert(TE % VEC == 0 && HC % 4 == 0, "pieces");
-    __shared__ __attribute__((aligned(16))) float s_x[2][TT][HP];
-    __shared__ __attribute__((aligned(16))) float s_w[2][TE][HP];
+    constexpr int WPR = EW / VEC;                    // 16-byte pieces per weight row (one h) of the workgroup
+    constexpr int XL = TT * XPR / kWave;             // token pieces per copy lane and chunk
+    constexpr int WG = HC / 4 * WPR / kWave;         // (4 rows, piece) groups per copy lane and chunk
+    static_assert(TT * TE == kWave, "one chain per lane");
+    static_assert(XL >= 1 && TT * XPR % kWave == 0 && WG >= 1 && HC / 4 * WPR % kWave == 0, "chunk split");
+    static_assert(EW % VEC == 0 && HC % 4 == 0, "pieces");
+    __shared__ __attribute__((aligned(16))) float s_x[NB][TT][HP];
+    __shared__ __attribute__((aligned(16))) float s_w[NB][EW][HP];
     if (static_cast<int>(blockIdx.x) >= ntile) {
         cache_region(pf, pf_units, blockIdx.x - ntile, gridDim.x - ntile, &s_x[0][0][0]);
         return;
     }
-    const int tid = threadIdx.x;
-    const int net = (E + TE - 1) / TE;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int net = (E + EW - 1) / EW;
     const int tok0 = (static_cast<int>(blockIdx.x) / net) * TT;
-    const int e0 = (static_cast<int>(blockIdx.x) % net) * TE;
+    const int e0 = (static_cast<int>(blockIdx.x) % net) * EW;
     const int nc = H / HC;
 
-    // a ring of RD chunks in registers: chunk c sits in slot c % RD, loaded RD - 1 chunks ahead
-    u32x4 xr[RD][XL], wr[RD][WL];
-    // token rows past T repeat row T-1; weight pieces past E repeat the last piece (both unused)
-    auto load = [&](int c, int q) {
-        const int h0 = c * HC;
+    if (wave == CH) {
+        // ---- copy wave: chunk c sits in register slot c & 1 from one chunk before it is stored
+        u32x4 xr[2][XL], wr[2][WG][4];
+        // token rows past T repeat row T-1; weight pieces past E repeat the last piece (both unused)
+        auto load = [&](int c, auto qc) {
+            constexpr int q = decltype(qc)::value;
+            const int h0 = c * HC;
 #pragma unroll
-        for (int j = 0; j < XL; ++j) {
-            const int i = j * NT + tid;
-            const int t = min(tok0 + i / XPR, T - 1);
-            xr[q][j] = *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t) * H + h0 + (i % XPR) * VEC);
+            for (int j = 0; j < XL; ++j) {
+                const int i = j * kWave + lane;
+                const int t = min(tok0 + i / XPR, T - 1);
+                xr[q][j] = *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t) * H + h0 + (i % XPR) * VEC);
+            }
+#pragma unroll
+            for (int j = 0; j < WG; ++j) {
+                const int g = j * kWave + lane;          // rows 4 (g / WPR) .. +3, piece g % WPR
+                const int ec = min(e0 + (g % WPR) * VEC, E - VEC);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    wr[q][j][r] = *reinterpret_cast<const u32x4*>(
+                        w + static_cast<int64_t>(h0 + 4 * (g / WPR) + r) * E + ec);
+            }
+        };
+        auto widen = [](const u32x4& r, int v) -> float {
+            if constexpr (sizeof(XT) == 2) {
+                const uint32_t u = r[v >> 1];
+                return __uint_as_float((v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+            } else {
+                return __uint_as_float(r[v]);
+            }
+        };
+        auto store = [&](int b, auto qc) {
+            constexpr int q = decltype(qc)::value;
+#pragma unroll
+            for (int j = 0; j < XL; ++j) {
+                const int i = j * kWave + lane;
+                float* dst = &s_x[b][i / XPR][(i % XPR) * VEC];
+#pragma unroll
+                for (int v = 0; v < VEC; v += 4)
+                    *reinterpret_cast<floatx4*>(dst + v) = floatx4{widen(xr[q][j], v), widen(xr[q][j], v + 1),
+                                                                   widen(xr[q][j], v + 2), widen(xr[q][j], v + 3)};
+            }
+#pragma unroll
+            for (int j = 0; j < WG; ++j) {
+                const int g = j * kWave + lane;
+                const int hr = 4 * (g / WPR), col = (g % WPR) * VEC;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+                    *reinterpret_cast<floatx4*>(&s_w[b][col + v][hr]) =
+                        floatx4{widen(wr[q][j][0], v), widen(wr[q][j][1], v), widen(wr[q][j][2], v),
+                                widen(wr[q][j][3], v)};
+            }
+        };
+        load(0, std::integral_constant<int, 0>());
+        if (nc > 1) load(1, std::integral_constant<int, 1>());
+        store(0, std::integral_constant<int, 0>());
+        if (nc > 1) store(1, std::integral_constant<int, 1>());
+        if (nc > 2) load(2, std::integral_constant<int, 0>());
+        __syncthreads();                             // chunks 0 and 1 are in LDS
+        // chunk c: store chunk c + 2 into the buffer chunk c - 1 used, load chunk c + 3 into the
+        // register slot chunk c + 1 left
+        for (int c0 = 0; c0 < nc; c0 += 2) {
+            static_for<2>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                const int c = c0 + q;
+                if (c < nc) {
+                    if (c + 2 < nc) store((c + 2) % NB, std::integral_constant<int, q>());
+                    if (c + 3 < nc) load(c + 3, std::integral_constant<int, 1 - q>());
+                    __syncthreads();
+                }
+            });
         }
-#pragma unroll
-        for (int j = 0; j < WL; ++j) {
-            const int i = j * NT + tid;
-            const int ec = min(e0 + (i % WPR) * VEC, E - VEC);
-            wr[q][j] = *reinterpret_cast<const u32x4*>(w + static_cast<int64_t>(h0 + i / WPR) * E + ec);
-        }
-    };
-    auto widen = [](const u32x4& r, int v) -> float {
-        if constexpr (sizeof(XT) == 2) {
-            const uint32_t u = r[v >> 1];
-            return __uint_as_float((v & 1) ? (u & 0xFFFF0000u) : (u << 16));
-        } else {
-            return __uint_as_float(r[v]);
-        }
-    };
-    auto store = [&](int b, int q) {
-#pragma unroll
-        for (int j = 0; j < XL; ++j) {
-            const int i = j * NT + tid;
-            float* dst = &s_x[b][i / XPR][(i % XPR) * VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; v += 4)
-                *reinterpret_cast<floatx4*>(dst + v) = floatx4{widen(xr[q][j], v), widen(xr[q][j], v + 1),
-                                                               widen(xr[q][j], v + 2), widen(xr[q][j], v + 3)};
-        }
-#pragma unroll
-        for (int j = 0; j < WL; ++j) {
-            const int i = j * NT + tid;
-            const int hr = i / WPR, g = i % WPR;
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) s_w[b][g * VEC + v][hr] = widen(wr[q][j], v);
-        }
-    };
+        return;
+    }
 
-    const int tl = tid / TE, el = tid % TE;
+    // ---- chain waves
+    const int tl = lane / TE, el = wave * TE + lane % TE;
     float acc = 0.0f;
-#pragma unroll
-    for (int q = 0; q < RD; ++q)
-        if (q < nc) load(q, q);
-    store(0, 0);
-    __syncthreads();
-    // chunk c: run the chains over LDS buffer c & 1, widen chunk c+1 into the other buffer (the one
-    // chunk c-1 used: everyone passed the last barrier), load chunk c+RD into the slot chunk c left
-    auto chunk = [&](int c, auto qc) {
-        constexpr int q = decltype(qc)::value;
-        const int b = c & 1;
+    __syncthreads();                                 // chunks 0 and 1 are in LDS
+    for (int c = 0; c < nc; ++c) {
+        const int b = c % NB;
         const float* px = s_x[b][tl];
         const float* pw = s_w[b][el];
 #pragma unroll 8
@@ -700,14 +746,7 @@ __global__ __launch_bounds__(TT * TE) void route_tile_kernel(
             acc = __builtin_fmaf(xv[2], wv[2], acc);
             acc = __builtin_fmaf(xv[3], wv[3], acc);
         }
-        if (c + 1 < nc) store(b ^ 1, (q + 1) % RD);
-        if (c + RD < nc) load(c + RD, q);
-        __syncthreads();
-    };
-    for (int c0 = 0; c0 < nc; c0 += RD) {
-        static_for<RD>([&](auto qc) {
-            if (c0 + decltype(qc)::value < nc) chunk(c0 + decltype(qc)::value, qc);
-        });
+        __syncthreads();                             // chunk c + 1 is complete; buffer b may be refilled
     }
     const int t = tok0 + tl, e = e0 + el;
     if (t < T && e < E) {
@@ -773,10 +812,10 @@ void launch_chain(const moe_shape& s, const XT* x, const XT* w, const float* bia
                        static_cast<const uint16_t*>(pf.region), static_cast<int64_t>(pf.bytes / 1024));
 }
 
-constexpr int kTileTokens = 8;      // tiled router: tokens x experts per workgroup (one wave), h per chunk
+constexpr int kTileTokens = 8;      // tiled router: tokens x experts per chain wave, h per chunk
 constexpr int kTileExperts = 8;
+constexpr int kTileChains = 1;      // chain waves per workgroup (beside one copy wave)
 constexpr int kTileChunk = 256;
-constexpr int kTileRing = 2;        // chunks in flight through registers
 constexpr int kTileMaxT = 1024;
 
 bool tile_eligible(const moe_shape& s, int x_dtype) {
@@ -787,11 +826,12 @@ bool tile_eligible(const moe_shape& s, int x_dtype) {
 template <typename XT>
 void launch_tile(const moe_shape& s, const XT* x, const XT* w, const float* bias, float* logits, int32_t* idx,
                  float* tw, const CachePrefetch& pf, hipStream_t st) {
-    const int ntile = ((s.T + kTileTokens - 1) / kTileTokens) * ((s.E + kTileExperts - 1) / kTileExperts);
+    constexpr int EW = kTileChains * kTileExperts;
+    const int ntile = ((s.T + kTileTokens - 1) / kTileTokens) * ((s.E + EW - 1) / EW);
     const int extra = prefetch_workgroups(ntile, pf);
-    hipLaunchKernelGGL((route_tile_kernel<XT, kTileTokens, kTileExperts, kTileChunk, kTileRing>), dim3(ntile + extra),
-                       dim3(kTileTokens * kTileExperts), 0, st, x, w, bias, s.T, s.H, s.E, logits, ntile,
-                       static_cast<const uint16_t*>(pf.region), static_cast<int64_t>(pf.bytes / 1024));
+    hipLaunchKernelGGL((route_tile_kernel<XT, kTileTokens, kTileExperts, kTileChains, kTileChunk>),
+                       dim3(ntile + extra), dim3((kTileChains + 1) * kWave), 0, st, x, w, bias, s.T, s.H, s.E,
+                       logits, ntile, static_cast<const uint16_t*>(pf.region), static_cast<int64_t>(pf.bytes / 1024));
     launch_route_from_logits(s, logits, idx, tw, st);
 }
 
