@@ -446,9 +446,16 @@ int moe_layer_mxfp8(const moe_shape* s, const void* x, int x_dtype, const void* 
     MOE_TRY(launch_route_prefetch(*s, x, x_dtype, w_router, bias, idx, tw, nullptr, w.route_scratch, w.route_bytes,
                                   st, pf));
     MOE_TRY(launch_mx_quantize(s->T, s->H, x, x_dtype, w.x_codes, w.x_scales, st));
-    MOE_TRY(launch_dispatch(*s, idx, nullptr, x_dtype, cnt, off, rt, rs, sr, nullptr, w.dispatch_scratch, st));
-    MOE_TRY(launch_mx_grouped_gemm(*s, w.x_codes, w.x_scales, rt, off, pk, MOE_GEMM_GATE_UP, MOE_EPI_SWIGLU,
-                                   w.h_codes, MOE_MXFP8, w.h_scales, st));
+    if (mx_gemm_can_derive_dispatch(*s)) {
+        // few rows per expert: the weight-streaming gate/up GEMM derives the
+        // dispatch itself (one launch fewer) and writes its outputs on the way
+        MOE_TRY(launch_mx_gate_up_deriving_dispatch(*s, w.x_codes, w.x_scales, idx, pk, w.h_codes, w.h_scales, cnt,
+                                                    off, rt, rs, sr, st));
+    } else {
+        MOE_TRY(launch_dispatch(*s, idx, nullptr, x_dtype, cnt, off, rt, rs, sr, nullptr, w.dispatch_scratch, st));
+        MOE_TRY(launch_mx_grouped_gemm(*s, w.x_codes, w.x_scales, rt, off, pk, MOE_GEMM_GATE_UP, MOE_EPI_SWIGLU,
+                                       w.h_codes, MOE_MXFP8, w.h_scales, st));
+    }
     MOE_TRY(launch_mx_grouped_gemm(*s, w.h_codes, w.h_scales, nullptr, off, pk, MOE_GEMM_DOWN, MOE_EPI_NONE, w.y,
                                    MOE_F16, nullptr, st));
     MOE_TRY(launch_combine(*s, w.y, MOE_F16, sr, tw, out, st));

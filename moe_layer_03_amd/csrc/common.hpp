@@ -163,6 +163,17 @@ int launch_mx_quantize(int64_t rows, int K, const void* x, int x_dtype, uint8_t*
                        hipStream_t st);
 // Whether launch_mx_grouped_gemm takes its weight-streaming form.
 bool mx_gemm_streams_weights(const moe_shape& s);
+// Whether the gate/up launch below applies (weight streaming, at most 1024
+// tokens and 1024 local experts, offsets within the buffer range).
+bool mx_gemm_can_derive_dispatch(const moe_shape& s);
+// Weight-streaming MXFP8 gate/up GEMM with the SwiGLU epilogue (MXFP8 h) that
+// reads the quantised token rows [T][H] directly, derives the dispatch from
+// topk_idx itself and writes the dispatch outputs on the way: dispatch and
+// gate/up in one launch.
+int launch_mx_gate_up_deriving_dispatch(const moe_shape& s, const uint8_t* x_codes, const uint8_t* x_scales,
+                                        const int32_t* topk_idx, const uint8_t* packed, uint8_t* h_codes,
+                                        uint8_t* h_scales, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                        int32_t* row_slot, int32_t* slot_row, hipStream_t st);
 int launch_mx_grouped_gemm(const moe_shape& s, const uint8_t* a, const uint8_t* a_scales, const int32_t* a_rows,
                            const int32_t* offsets, const uint8_t* packed, int which, int epilogue, void* c,
                            int c_dtype, uint8_t* c_scales, hipStream_t st);

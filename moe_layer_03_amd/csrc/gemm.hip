@@ -99,8 +99,6 @@ struct GemmArgs {
     int32_t* d_slot_row;
 };
 
-constexpr int kDeriveMaxT = 1024;      // tokens of a derived dispatch (one expert's row list in LDS)
-constexpr int kDeriveMaxE = 1024;
 
 __device__ __forceinline__ int swz(int row, int kg) {
     // Swizzled granule position of logical granule kg (0..3) of a 64-byte row.
@@ -349,68 +347,6 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 // tiles are added in wave order through LDS by all threads, which then apply
 // the epilogue.
 // ---------------------------------------------------------------------------
-// The dispatch of expert e derived in the workgroup from the routing: the
-// histogram of local experts gives the expert's first row (the exclusive sum
-// over the experts before it) and row count, and an order-keeping compaction of
-// the (token, slot) entries routed to e lists its rows by ascending token (a
-// token lists an expert once), the stable order of the dispatch.  The first
-// column block of every expert writes that expert's part of the dispatch
-// outputs; expert 0's also writes the total and -1 for non-local slots.
-__device__ void derive_dispatch(const GemmArgs& p, int e, int nb, int* s_cnt, int* s_list, int* s_w4, int& seg0,
-                                int& rows) {
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1), wave = tid >> 6;
-    for (int i = tid; i < p.E_loc; i += 256) s_cnt[i] = 0;
-    __syncthreads();
-    const int n = p.T * p.K;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int run = 0;                                       // entries of e listed so far (uniform)
-    for (int base = 0; base < n; base += 256) {
-        const int i = base + tid;
-        int v = -1;
-        if (i < n) {
-            v = p.topk_idx[i] - p.e_begin;
-            if (v >= 0 && v < p.E_loc) atomicAdd(&s_cnt[v], 1);
-        }
-        const bool mine = v == e;
-        const uint64_t m = __ballot(mine);
-        if (lane == 0) s_w4[wave] = __popcll(m);
-        __syncthreads();
-        int wb = 0;
-        for (int w = 0; w < wave; ++w) wb += s_w4[w];
-        const int tot = s_w4[0] + s_w4[1] + s_w4[2] + s_w4[3];
-        if (mine) s_list[run + wb + __popcll(m & below)] = i;
-        run += tot;
-        __syncthreads();                               // s_w4 reuse
-    }
-    rows = s_cnt[e];
-    int part = 0;
-    for (int k = tid; k < e; k += 256) part += s_cnt[k];
-    seg0 = block_sum256(part, s_w4);
-    if (nb != 0) return;
-    if (tid == 0) {
-        p.d_counts[e] = rows;
-        p.d_offsets[e] = seg0;
-    }
-    for (int r = tid; r < rows; r += 256) {
-        const int i = s_list[r];
-        const int t = i / p.K;
-        p.d_row_token[seg0 + r] = t;
-        p.d_row_slot[seg0 + r] = i - t * p.K;
-        p.d_slot_row[i] = seg0 + r;
-    }
-    if (e == 0) {
-        int all = 0;
-        for (int k = tid; k < p.E_loc; k += 256) all += s_cnt[k];
-        all = block_sum256(all, s_w4);
-        if (tid == 0) p.d_offsets[p.E_loc] = all;
-        for (int i = tid; i < n; i += 256) {
-            const int v = p.topk_idx[i] - p.e_begin;
-            if (v < 0 || v >= p.E_loc) p.d_slot_row[i] = -1;
-        }
-    }
-}
-
 template <int MODE, bool F16, int OUT, int BD>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_skinny_kernel(GemmArgs p) {
     typedef typename OutType<OUT>::type OutT;

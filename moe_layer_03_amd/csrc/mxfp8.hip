@@ -179,6 +179,15 @@ struct MxArgs {
     void* c;                   // output rows (codes for kMxOutMX)
     uint8_t* c_scales;         // kMxOutMX: [rows][ldc/32]
     int E_loc, N, Kd, ldc, I;
+    // weight-streaming gate/up only, optional: derive the dispatch from the
+    // routing instead of reading offsets / a_rows (a holds the T token rows)
+    const int32_t* topk_idx;   // [T][K] expert ids, NULL: not derived
+    int e_begin, T, K;
+    int32_t* d_counts;         // dispatch outputs, written by each expert's first column block
+    int32_t* d_offsets;
+    int32_t* d_row_token;
+    int32_t* d_row_slot;
+    int32_t* d_slot_row;
 };
 
 // One 16-byte-per-lane buffer -> LDS copy (lane l lands at base + 16 l).
@@ -539,11 +548,22 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_mx_skinny_kernel(MxArgs p
             sb[slot][t] = __builtin_amdgcn_raw_buffer_load_b8(bs_rsrc, bs_base[t] + 2 * ks, 0, 0);
         }
     };
+    // the first ring of weight loads needs no routing data: it is in flight
+    // while the expert's row range and row indices are read (or derived)
 #pragma unroll
     for (int j = 0; j < BD; ++j) load_b(j, j);
 
-    const int seg0 = p.offsets[e];
-    const int rows = p.offsets[e + 1] - seg0;
+    __shared__ int s_cnt[kDeriveMaxE];
+    __shared__ int s_list[kDeriveMaxT];
+    __shared__ int s_w4[4];
+    const bool derived = p.topk_idx != nullptr;        // uniform
+    int seg0, rows;
+    if (derived) {
+        derive_dispatch(p, e, nb, s_cnt, s_list, s_w4, seg0, rows);
+    } else {
+        seg0 = p.offsets[e];
+        rows = p.offsets[e + 1] - seg0;
+    }
     if (rows <= 0) {
 #pragma unroll
         for (int j = 0; j < BD; ++j)
@@ -563,7 +583,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_mx_skinny_kernel(MxArgs p
         for (int t = 0; t < MT; ++t) {
             const int rr = g0 + t * 32 + (lane & 31);
             const bool ok = rr < rows;
-            const int64_t src = ok ? (p.a_rows != nullptr ? p.a_rows[seg0 + rr] : seg0 + rr) : 0;
+            const int64_t src = !ok ? 0
+                                : derived ? s_list[rr] / p.K
+                                : (p.a_rows != nullptr ? p.a_rows[seg0 + rr] : seg0 + rr);
             a_off[t] = ok ? static_cast<uint32_t>(src * p.Kd + h * 16) : kOutOfRange;
             as_off[t] = ok ? static_cast<uint32_t>(src * kb32 + h) : kOutOfRange;
         }
@@ -756,6 +778,46 @@ int launch_mx_quantize(int64_t rows, int K, const void* x, int x_dtype, uint8_t*
 
 bool mx_gemm_streams_weights(const moe_shape& s) {
     return static_cast<int64_t>(s.T) * s.K <= static_cast<int64_t>(64) * s.E;
+}
+
+bool mx_gemm_can_derive_dispatch(const moe_shape& s) {
+    return mx_gemm_streams_weights(s) && s.H % 256 == 0 && s.T <= kDeriveMaxT && s.e_end - s.e_begin <= kDeriveMaxE &&
+           static_cast<int64_t>(s.T) * s.H + 64 <= kBufferRange &&
+           static_cast<int64_t>(s.e_end - s.e_begin) * 2 * s.I * s.H + 4096 <= kBufferRange;
+}
+
+int launch_mx_gate_up_deriving_dispatch(const moe_shape& s, const uint8_t* x_codes, const uint8_t* x_scales,
+                                        const int32_t* topk_idx, const uint8_t* packed, uint8_t* h_codes,
+                                        uint8_t* h_scales, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                        int32_t* row_slot, int32_t* slot_row, hipStream_t st) {
+    if (!mx_gemm_can_derive_dispatch(s)) return MOE_ERR_UNSUPPORTED;
+    MxArgs args{};
+    args.a = x_codes;
+    args.a_scales = x_scales;
+    args.a_rows_bound = s.T;
+    args.c = h_codes;
+    args.c_scales = h_scales;
+    args.E_loc = s.e_end - s.e_begin;
+    args.I = s.I;
+    args.b = packed;
+    args.b_scales = packed + mx_packed_gate_up_code_bytes(s) + mx_packed_down_code_bytes(s);
+    args.N = 2 * s.I;
+    args.Kd = s.H;
+    args.ldc = s.I;
+    args.topk_idx = topk_idx;
+    args.e_begin = s.e_begin;
+    args.T = s.T;
+    args.K = s.K;
+    args.d_counts = counts;
+    args.d_offsets = offsets;
+    args.d_row_token = row_token;
+    args.d_row_slot = row_slot;
+    args.d_slot_row = slot_row;
+    const int64_t grid = static_cast<int64_t>(args.E_loc) * (args.N / 64);
+    hipLaunchKernelGGL((grouped_gemm_mx_skinny_kernel<kSwiGLU, kMxOutMX, 2>), dim3(static_cast<unsigned>(grid)),
+                       dim3(256), 0, st, args);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
 }
 
 int launch_mx_grouped_gemm(const moe_shape& s, const uint8_t* a, const uint8_t* a_scales, const int32_t* a_rows,

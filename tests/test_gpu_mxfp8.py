@@ -189,6 +189,8 @@ MID = [
     W.Workload("mx_mid", T=700, H=512, E=32, K=4, I=256, e_begin=8, e_end=24, dtype="bf16"),
     W.Workload("mx_f32", T=301, H=256, E=16, K=3, I=256, e_begin=0, e_end=16, dtype="f32"),
     W.Workload("mx_small_batch", T=96, H=512, E=64, K=8, I=256, e_begin=0, e_end=8, dtype="bf16"),
+    # few rows per expert with local experts 24..39: the gate/up launch derives the dispatch itself
+    W.Workload("mx_small_offset", T=130, H=512, E=64, K=6, I=256, e_begin=24, e_end=40, dtype="bf16"),
     W.Workload("mx_skewed", T=900, H=256, E=64, K=6, I=256, e_begin=0, e_end=16, dtype="bf16", zipf_s=1.1),
 ]
 
