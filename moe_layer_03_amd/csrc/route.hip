@@ -1109,15 +1109,23 @@ __global__ __launch_bounds__(256) void route_screen_kernel(
     }
 }
 
+// Largest value over each row of 16 lanes, in every lane of the row: a running
+// maximum by DPP row shifts (lanes shifted in from outside the row see 0,
+// neutral for an unsigned maximum), then lane 15's result broadcast to its row.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x15F, 0xf, 0xf, false));
+}
+
+// Largest 64-bit value over each row of 16 lanes: the largest upper half, then
+// the largest lower half among the lanes holding it.
 __device__ __forceinline__ uint64_t group16_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 16);
-        uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 16);
-        uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    const uint32_t hi = row16_max_u32(static_cast<uint32_t>(v >> 32));
+    const uint32_t lo = row16_max_u32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // 256-byte rows (128 bf16): the 16 rows one ds_read_b128 pass reads at one
