@@ -251,14 +251,15 @@ def measure(wl, steps, warmup, graph, copy_probe_mib=0):
     per_step = np.array([ev_f[k].elapsed_time(ev_f[k + 1]) for k in range(steps)])
 
     # second timed region: the same K steps through the staged entry points, with HIP events around every
-    # stage on the launch stream (per-stage durations and the dominant kernel's roofline)
+    # stage on the launch stream (per-stage durations and the dominant kernel's roofline); each step is queued
+    # behind a spin, so the events time the GPU's work, not the host's launches
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    prime = queue_primer(torch, step)
     for k in range(steps):
+        prime()
         step(events[k])
     torch.cuda.synchronize()
-    ms_staged = (time.perf_counter() - t0) * 1e3 / steps
+    ms_staged = float(np.mean([events[k][0].elapsed_time(events[k][-1]) for k in range(steps)]))
     stage_ms = {name: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(steps)]))
                 for i, name in enumerate(stages)}
 
@@ -323,6 +324,27 @@ def measure(wl, steps, warmup, graph, copy_probe_mib=0):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res, inp
+
+
+def queue_primer(torch, step):
+    """Returns a function that, called before `step()`, keeps the GPU busy (a torch.cuda._sleep spin) for
+    about three times the host time that enqueuing one step takes.  The step's kernels are then all queued
+    when the GPU reaches them, so HIP events between its stages time GPU execution, not the host's launch
+    latency (staged calls from Python can otherwise leave the GPU idle between stages)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1 << 20)
+    e1.record()
+    torch.cuda.synchronize()
+    cycles_per_us = (1 << 20) / max(e0.elapsed_time(e1) * 1e3, 1e-3)
+    host = []
+    for _ in range(3):
+        t = time.perf_counter()
+        step()
+        host.append(time.perf_counter() - t)
+    torch.cuda.synchronize()
+    cycles = int(3 * max(host) * 1e6 * cycles_per_us)
+    return lambda: torch.cuda._sleep(cycles)
 
 
 def measure_mxfp8(wl, steps, warmup, copy_probe_mib=0):
@@ -403,7 +425,9 @@ def measure_mxfp8(wl, steps, warmup, copy_probe_mib=0):
     ms = (time.perf_counter() - t0) * 1e3 / steps
     per = np.array([ev_f[k].elapsed_time(ev_f[k + 1]) for k in range(steps)])
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    prime = queue_primer(torch, staged)
     for k in range(steps):
+        prime()
         staged(evs[k])
     torch.cuda.synchronize()
     stage_ms = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
