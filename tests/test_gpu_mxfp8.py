@@ -219,3 +219,33 @@ def test_mxfp8_rejects_unsupported_shapes(B):
                           torch.zeros(256, dtype=torch.uint8, device="cuda"), ws=torch.zeros(256, dtype=torch.uint8,
                                                                                              device="cuda"))
     assert ei.value.status in (B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE)
+
+
+@pytest.mark.parametrize("wl", MID + [W.WORKLOADS["decode_ep16_shard"], W.WORKLOADS["prefill_ep4_shard"]],
+                         ids=lambda w: w.name)
+def test_layer_mxfp8_equals_staged_calls(B, wl):
+    """The fused MXFP8 entry point against the staged entry points in the same
+    order, bit for bit.  With few rows per expert the fused layer's
+    weight-streaming gate/up derives the dispatch itself, while the staged calls
+    dispatch with moe_dispatch and gather rows through row_token; the fused
+    layer's router works in its workspace (tiled below 1024 tokens, screened
+    above), like the staged call given one."""
+    inp = W.make_inputs(wl)
+    s = B.Shape.of(wl)
+    x, wr = to_torch(inp.x), to_torch(inp.w_router)
+    bias = to_torch(inp.bias) if inp.bias is not None else None
+    g, u, d = to_torch(inp.w_gate), to_torch(inp.w_up), to_torch(inp.w_down)
+    packed = B.moe_pack_weights_mxfp8(s, g, u, d)
+    torch.cuda.synchronize()
+    del g, u, d
+    fused = B.moe_layer_mxfp8(s, x, wr, packed, bias)
+    ws = torch.empty(max(B.moe_route_workspace_bytes(s), 16), dtype=torch.uint8, device="cuda")
+    idx, tw, _ = B.moe_route(s, x, wr, bias, ws=ws)
+    xc, xs = B.moe_quantize_mxfp8(x)
+    dd = B.moe_dispatch(s, idx, None)
+    hc, hs = B.moe_grouped_gemm_mxfp8(s, xc, xs, dd["offsets"], packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_SWIGLU,
+                                      c_dtype=torch.uint8, a_rows=dd["row_token"])
+    y = B.moe_grouped_gemm_mxfp8(s, hc, hs, dd["offsets"], packed, B.MOE_GEMM_DOWN, B.MOE_EPI_NONE)
+    out = B.moe_combine(s, y, dd["slot_row"], tw)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), fused.cpu().numpy()), "fused and staged MXFP8 outputs differ"
