@@ -97,9 +97,23 @@ constexpr int kDeriveMaxE = 1024;
 // column block of every expert writes that expert's part of the dispatch
 // outputs; expert 0's also writes the total and -1 for non-local slots.
 // Args carries topk_idx, e_begin, T, K, E_loc and the d_* outputs; 256 threads.
+// Routing entries 256 * q + tid for q < kDerivePrefetch, loaded before the
+// weight ring so that the waits for them do not also wait for the ring (vector
+// loads complete in order).  Entries past T * K read e_begin - 1 (not local).
+constexpr int kDerivePrefetch = 8;
+template <typename Args>
+__device__ __forceinline__ void derive_prefetch(const Args& p, int (&pre)[kDerivePrefetch]) {
+    const int n = p.T * p.K;
+#pragma unroll
+    for (int q = 0; q < kDerivePrefetch; ++q) {
+        const int i = q * 256 + static_cast<int>(threadIdx.x);
+        pre[q] = i < n ? p.topk_idx[i] : p.e_begin - 1;
+    }
+}
+
 template <typename Args>
 __device__ void derive_dispatch(const Args& p, int e, int nb, int* s_cnt, int* s_list, int* s_w4, int& seg0,
-                                int& rows) {
+                                int& rows, const int (&pre)[kDerivePrefetch]) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid >> 6;
     for (int i = tid; i < p.E_loc; i += 256) s_cnt[i] = 0;
@@ -107,13 +121,10 @@ __device__ void derive_dispatch(const Args& p, int e, int nb, int* s_cnt, int* s
     const int n = p.T * p.K;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int run = 0;                                       // entries of e listed so far (uniform)
-    for (int base = 0; base < n; base += 256) {
+    auto batch = [&](int base, int raw) {
         const int i = base + tid;
-        int v = -1;
-        if (i < n) {
-            v = p.topk_idx[i] - p.e_begin;
-            if (v >= 0 && v < p.E_loc) atomicAdd(&s_cnt[v], 1);
-        }
+        const int v = raw - p.e_begin;                 // entries past n read e_begin - 1: v = -1
+        if (v >= 0 && v < p.E_loc) atomicAdd(&s_cnt[v], 1);
         const bool mine = v == e;
         const uint64_t m = __ballot(mine);
         if (lane == 0) s_w4[wave] = __popcll(m);
@@ -124,6 +135,13 @@ __device__ void derive_dispatch(const Args& p, int e, int nb, int* s_cnt, int* s
         if (mine) s_list[run + wb + __popcll(m & below)] = i;
         run += tot;
         __syncthreads();                               // s_w4 reuse
+    };
+#pragma unroll
+    for (int q = 0; q < kDerivePrefetch; ++q)
+        if (q * 256 < n) batch(q * 256, pre[q]);
+    for (int base = kDerivePrefetch * 256; base < n; base += 256) {
+        const int i = base + tid;
+        batch(base, i < n ? p.topk_idx[i] : p.e_begin - 1);
     }
     rows = s_cnt[e];
     int part = 0;

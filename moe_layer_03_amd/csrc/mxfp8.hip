@@ -548,18 +548,21 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_mx_skinny_kernel(MxArgs p
             sb[slot][t] = __builtin_amdgcn_raw_buffer_load_b8(bs_rsrc, bs_base[t] + 2 * ks, 0, 0);
         }
     };
-    // the first ring of weight loads needs no routing data: it is in flight
-    // while the expert's row range and row indices are read (or derived)
+    // routing entries first (a derived dispatch), then the first ring of weight
+    // loads, which needs no routing data: it is in flight while the expert's
+    // row range and row indices are read or derived
+    const bool derived = p.topk_idx != nullptr;        // uniform
+    int pre[kDerivePrefetch];
+    if (derived) derive_prefetch(p, pre);
 #pragma unroll
     for (int j = 0; j < BD; ++j) load_b(j, j);
 
     __shared__ int s_cnt[kDeriveMaxE];
     __shared__ int s_list[kDeriveMaxT];
     __shared__ int s_w4[4];
-    const bool derived = p.topk_idx != nullptr;        // uniform
     int seg0, rows;
     if (derived) {
-        derive_dispatch(p, e, nb, s_cnt, s_list, s_w4, seg0, rows);
+        derive_dispatch(p, e, nb, s_cnt, s_list, s_w4, seg0, rows, pre);
     } else {
         seg0 = p.offsets[e];
         rows = p.offsets[e + 1] - seg0;
