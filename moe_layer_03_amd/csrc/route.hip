@@ -15,10 +15,11 @@
 // issues little besides v_fma.  Large bf16 batches with scratch screen the
 // experts with MFMA estimates and run the chains of the candidates only; other
 // large batches give each wave 3 tokens x all experts; small batches with
-// scratch give each one-wave workgroup a tile of 8 tokens x 8 experts (the
-// chain length sets their time), without scratch each wave 1 token x 64
-// experts.  Larger E uses the generic kernel.  Selection happens in registers
-// with wave-wide 64-bit max reductions over (orderable logit, ~expert) keys.
+// scratch give each workgroup's chain wave a tile of 8 tokens x 8 experts, fed
+// by a copy wave beside it (the chain length sets their time), without
+// scratch each wave 1 token x 64 experts.  Larger E uses the generic kernel.
+// Selection happens in registers over (orderable logit, ~expert) keys: the
+// largest key of a wave or a 16-lane row by DPP row shifts, ties by ballot.
 #include "common.hpp"
 #include "route_prefetch.hpp"
 
