@@ -134,12 +134,11 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
     constexpr int UM = 2 * BM;                         // rows per tile: two 128-row slabs
     constexpr int TM = BM / 32;                        // 32-row MFMA tiles per wave
     constexpr int KS = BK / 16;                        // MFMA k-steps per stage
-    constexpr int A_GRAN = UM * KG;                    // 16-byte granules of one A stage
-    constexpr int A_DMA = A_GRAN / NTHREADS;           // A copies per thread per stage
+    constexpr int A_BLKS = BM / 16;                    // 16-row copy blocks of one row half
+    constexpr int A_DMA = A_BLKS / WN;                 // A copies per thread per stage, at most
     constexpr int B_BLK = 2 * KS;                      // B blocks per wave column per stage
     constexpr int B_DMA = B_BLK * WN / NWAVES;         // B copies per thread per stage
-    constexpr int LOADS = A_DMA + B_DMA;               // vector-memory operations per thread per stage
-    static_assert(A_GRAN % NTHREADS == 0 && (B_BLK * WN) % NWAVES == 0, "stage must split evenly");
+    static_assert(A_BLKS % WN == 0 && (B_BLK * WN) % NWAVES == 0, "stage must split evenly");
 
     __shared__ __attribute__((aligned(16))) uint16_t s_a[NB][UM * BK];
     __shared__ __attribute__((aligned(16))) uint16_t s_b[NB][WN][B_BLK][kFragElems];
@@ -187,14 +186,16 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
         const bool active = my_rows > 0;
         const int na = min(TM, (my_rows + 31) >> 5);   // 32-row MFMA tiles holding valid rows
 
-        // A copies of this thread: LDS granule slot (i * NWAVES + wave) * 64 + lane holds
+        // A copies of this thread: the waves of a row half copy that half's rows (only
+        // its waves read them), copy i of column quarter nq moving 16-row block
+        // blk = mh * A_BLKS + i * WN + nq.  LDS granule slot blk * 64 + lane holds
         // swizzled position (row, g'); the swizzle is an involution, so the logical
         // granule is swz(row, g').  Rows past the segment copy the tile's first row
         // (never stored).  With a_rows the row is gathered from the unpacked input.
         const uint16_t* a_src[A_DMA];
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
-            const int slot = (i * NWAVES + wave) * 64 + lane;
+            const int slot = (mh * A_BLKS + i * WN + nq) * 64 + lane;
             const int row = slot / KG;
             const int kg = swz(row, slot % KG);
             const int r = row0 + (row < rows_valid ? row : 0);
@@ -210,10 +211,12 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
         for (int s2 = 0; s2 < 2; ++s2)
             b_src[s2] = p.b + frag_block(e, ((n_tile * BN + bq * 64) >> 5) + s2, 0, p.N, kblocks) * kFragElems +
                         lane * 8;
-        // issue the copies of k-tile kt into ring stage st
-        auto issue = [&](int kt, int st) {
+        // issue the copies of k-tile kt into ring stage st: AC activation copies (the
+        // blocks that hold the half's active row groups) and the weight copies
+        auto issue = [&](auto ac, int kt, int st) {
+            constexpr int AC = decltype(ac)::value;
 #pragma unroll
-            for (int i = 0; i < A_DMA; ++i) dma16(a_src[i] + kt * BK, &s_a[st][(i * NWAVES + wave) * 64 * 8]);
+            for (int i = 0; i < AC; ++i) dma16(a_src[i] + kt * BK, &s_a[st][((mh * A_BLKS + i * WN + nq) * 64) * 8]);
 #pragma unroll
             for (int d = 0; d < B_DMA; ++d) {
                 const int j = jb + d;
@@ -228,16 +231,20 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-        // prologue: k-tiles 0 .. NB-2 in flight (indices past the end are clamped:
-        // harmless copies keep the per-stage operation count constant)
-#pragma unroll
-        for (int q = 0; q + 1 < NB; ++q) issue(min(q, nk - 1), q);
-
-        // The k-loop for NA active 32-row groups (0: an idle half that only copies
-        // and synchronises).  NA is fixed per tile, so a k-step is one basic block:
-        // its fragment reads and MFMAs interleave with no wait between reads.
+        // The k-loop for NA active 32-row groups (0: an idle half that copies only
+        // weights and synchronises).  NA is fixed per tile, so a k-step is one basic
+        // block: its fragment reads and MFMAs interleave with no wait between reads.
+        // A wave copies the activation blocks of its half's first NA row groups, so
+        // its copies per stage (LOADS) are fixed per instantiation too; each wave
+        // waits for its own copies before the barrier.
         auto kloop = [&](auto nac) {
             constexpr int NA = decltype(nac)::value;
+            constexpr int AC = (2 * NA + WN - 1) / WN < A_DMA ? (2 * NA + WN - 1) / WN : A_DMA;
+            constexpr int LOADS = AC + B_DMA;          // vector-memory operations per thread per stage
+            // prologue: k-tiles 0 .. NB-2 in flight (indices past the end are clamped:
+            // harmless copies keep the per-stage operation count constant)
+#pragma unroll
+            for (int q = 0; q + 1 < NB; ++q) issue(IntC<AC>{}, min(q, nk - 1), q);
             u32x4 fa_cur[TM], fb_cur[2], fa_nxt[TM], fb_nxt[2];
             auto read_frags = [&](u32x4 (&fa)[TM], u32x4 (&fb)[2], int st, int ks) {
                 const int kg = ks * 2 + (lane >> 5);
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(WN * 128, 1) void grouped_gemm_kernel(GemmArgs p) {
                 }
                 wait_vmcnt<LOADS * (NB - 3)>();
                 __builtin_amdgcn_s_barrier();
-                issue(min(kt + NB - 1, nk - 1), (st + NB - 1) % NB);
+                issue(IntC<AC>{}, min(kt + NB - 1, nk - 1), (st + NB - 1) % NB);
                 if constexpr (NA > 0) {
                     read_frags(fa_cur, fb_cur, (st + 1) % NB, 0);
                     __builtin_amdgcn_sched_barrier(0);

@@ -237,12 +237,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
     constexpr int NWAVES = 8, NTHREADS = 512, WN = 4, BM = 128, UM = 256, BN = 256, TM = 4;
     constexpr int A_STAGE = UM * 64;                  // bytes
     constexpr int B_STAGE = BN * 64;
-    constexpr int A_DMA = A_STAGE / 16 / NTHREADS;    // 2
+    constexpr int A_BLKS = BM / 16;                   // 16-row (1 KiB) copy blocks of one row half
+    constexpr int A_DMA = A_BLKS / WN;                // A copies per thread per stage, at most: 2
     constexpr int B_DMA = B_STAGE / 16 / NTHREADS;    // 2
-    constexpr int LOADS = A_DMA + B_DMA;              // copies per thread per stage
     constexpr int SG = 8;                             // k-steps per scale group
     constexpr int S_GROUP = (UM + BN) * 16;           // scale bytes of a group: 16 per A row and per B column
-    static_assert(NB == 4 && A_DMA == 2 && B_DMA == 2 && UM + BN == NTHREADS, "stage split");
+    static_assert(NB == 4 && A_DMA == 2 && B_DMA == 2 && A_STAGE == 2 * A_BLKS * 1024 && UM + BN == NTHREADS,
+                  "stage split");
     static_assert(SG % NB == 0, "a scale group spans whole turns of the ring");
     __shared__ __attribute__((aligned(1024))) uint8_t s_a[NB][A_STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t s_b[NB][B_STAGE];
@@ -295,11 +296,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
         const bool active = my_rows > 0;
         const int na = min(TM, (my_rows + 31) >> 5);
 
-        // A code copies: LDS granule slot (i * NWAVES + wave) * 64 + lane = (row, physical granule)
+        // A code copies: the waves of a row half copy that half's rows (only its waves
+        // read them), copy i of column quarter nq moving 16-row block
+        // blk = mh * A_BLKS + i * WN + nq; LDS granule slot blk * 64 + lane = (row, physical granule)
         uint32_t a_off[A_DMA];
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
-            const int slot = (i * NWAVES + wave) * 64 + lane;
+            const int slot = (mh * A_BLKS + i * WN + nq) * 64 + lane;
             const int row = slot >> 2;
             const int kg = (slot & 3) ^ ((row >> 2) & 3);
             uint32_t off = kOutOfRange;
@@ -335,10 +338,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
         } else {
             s_off = static_cast<uint32_t>((static_cast<int64_t>(e) * p.N + n_tile * BN + (tid - UM)) * kb32);
         }
-        auto issue = [&](int kt, int st) {
+        // the copies of k-tile kt into ring stage st: AC code copies of activations (the
+        // blocks that hold the half's active row groups) and the weight copies
+        auto issue = [&](auto ac, int kt, int st) {
+            constexpr int AC = decltype(ac)::value;
 #pragma unroll
-            for (int i = 0; i < A_DMA; ++i)
-                copy16_to_lds(a_rsrc, &s_a[st][(i * NWAVES + wave) * 64 * 16], a_off[i] + kt * kMxStepK);
+            for (int i = 0; i < AC; ++i)
+                copy16_to_lds(a_rsrc, &s_a[st][(mh * A_BLKS + i * WN + nq) * 64 * 16], a_off[i] + kt * kMxStepK);
 #pragma unroll
             for (int d = 0; d < B_DMA; ++d)
                 copy16_to_lds(b_rsrc, &s_b[st][(wave * B_DMA + d) * 1024], b_off[d] + kt * 2 * kMxTile);
@@ -359,12 +365,16 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-        issue_scales(0, 0);
-#pragma unroll
-        for (int q = 0; q + 1 < NB; ++q) issue(min(q, nk - 1), q);
-
+        // The k-loop for NA active 32-row groups.  A wave copies the activation blocks of
+        // its half's first NA row groups, so its copies per stage (LOADS) are fixed per
+        // instantiation; each wave waits for its own copies before the barrier.
         auto kloop = [&](auto nac) {
             constexpr int NA = decltype(nac)::value;
+            constexpr int AC = (2 * NA + WN - 1) / WN < A_DMA ? (2 * NA + WN - 1) / WN : A_DMA;
+            constexpr int LOADS = AC + B_DMA;          // copies per thread per stage
+            issue_scales(0, 0);
+#pragma unroll
+            for (int q = 0; q + 1 < NB; ++q) issue(IntC<AC>{}, min(q, nk - 1), q);
             // fragments of one k-step: A 2 x 16 bytes per row tile, B 2 x 16 bytes per column tile,
             // and the lane's scale bytes (row / column lane & 31, block h of the step).  B fragments
             // are double-buffered: the next stage's are read first, while this stage's MFMAs run; A
@@ -406,7 +416,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(MxArgs p) {
                 wait_vmcnt<q == 1 ? LOADS + 1 : LOADS>();
                 __builtin_amdgcn_s_barrier();          // ... everyone's; nobody reads stage kt - 1 any more
                 if constexpr (q == 0) issue_scales((kt / SG + 1) & 1, min(kt / SG + 1, ng - 1));
-                issue(min(kt + NB - 1, nk - 1), (st + NB - 1) % NB);
+                issue(IntC<AC>{}, min(kt + NB - 1, nk - 1), (st + NB - 1) % NB);
                 if constexpr (NA > 0) {
                     const int so = sc_off(kt + 1);
                     read_b(nbuf, nst, so);
