@@ -27,6 +27,10 @@
 //   * a stage is 32 k: 16 KiB of activations (256 rows x 64 bytes) and 16 KiB
 //     of weights (256 columns), 128 KiB for the ring; at the prefill shapes
 //     this copy path, not the MFMAs, sets the kernel's pace;
+//   * the waves of a row half copy that half's activation rows, and only the
+//     16-row blocks that hold its active 32-row groups (a 183-row tile copies
+//     192 rows per stage, not 256); the count is fixed per k-loop instance, so
+//     every copy wait stays a compile-time constant;
 //   * weights (B) are packed once in MFMA fragment order (one 1 KiB block per
 //     32 columns x 16 k, lane-major), the two 32-column halves of each
 //     64-column block side by side per 16 k: every copy and every fragment
