@@ -9,7 +9,8 @@
 // entries (at most K rows), adds w * y_row in ascending slot order in float32
 // and writes the whole output row once -- no atomics, deterministic.  Each
 // thread handles 8 consecutive features: one 16-byte bf16/fp16 load (or two
-// 16-byte float32 loads) per slot, two 16-byte float32 stores.  Small batches
+// 16-byte float32 loads) per slot, all slots' loads issued before the first
+// is summed (K <= 8), then two 16-byte float32 stores.  Small batches
 // give each workgroup one token and half of its features, so a few hundred
 // tokens still spread over the chip.
 #include "common.hpp"
@@ -19,6 +20,50 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTokensPerBlock = 2;
+constexpr int kMaxSlots = 8;        // local slots held in registers at once (K <= 8)
+
+// 8 consecutive features of one y row (16-bit or float32) as float32.
+template <typename YT, bool F16>
+struct RowChunk {
+    static constexpr int kWords = sizeof(YT) == 2 ? 4 : 8;
+    uint32_t v[kWords];
+    __device__ __forceinline__ void load(const YT* p) {
+        if constexpr (sizeof(YT) == 2) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) v[d] = a[d];
+        } else {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(p + 4);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                v[d] = a[d];
+                v[4 + d] = b[d];
+            }
+        }
+    }
+    // acc[i] = fma(w, feature i, acc[i])
+    __device__ __forceinline__ void accumulate(float w, float (&acc)[8]) const {
+        if constexpr (sizeof(YT) == 2) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                float lo, hi;
+                if constexpr (F16) {
+                    lo = f16_to_f32(static_cast<uint16_t>(v[d] & 0xFFFFu));
+                    hi = f16_to_f32(static_cast<uint16_t>(v[d] >> 16));
+                } else {
+                    lo = __uint_as_float(v[d] << 16);
+                    hi = __uint_as_float(v[d] & 0xFFFF0000u);
+                }
+                acc[2 * d] = fmaf(w, lo, acc[2 * d]);
+                acc[2 * d + 1] = fmaf(w, hi, acc[2 * d + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[d] = fmaf(w, __uint_as_float(v[d]), acc[d]);
+        }
+    }
+};
 
 template <typename YT, bool F16, int TPB>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict__ y, int T, int H, int K,
@@ -31,35 +76,39 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict_
     for (int q = 0; q < TPB; ++q) {
         const int t = blockIdx.x * TPB + q;
         if (t >= T) return;
-        for (int k = blockIdx.y * cw + threadIdx.x * 8; k < k_end; k += kThreads * 8) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        // the token's local slots in ascending slot order (uniform over the workgroup)
+        int rows[kMaxSlots];
+        float ws[kMaxSlots];
+        int nl = 0;
+        if (K <= kMaxSlots) {
             for (int j = 0; j < K; ++j) {
                 const int r = slot_row[static_cast<int64_t>(t) * K + j];
-                if (r < 0) continue;
-                const float w = topk_w[static_cast<int64_t>(t) * K + j];
-                if constexpr (sizeof(YT) == 2) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(r) * H + k);
+                if (r >= 0) {
+                    rows[nl] = r;
+                    ws[nl] = topk_w[static_cast<int64_t>(t) * K + j];
+                    ++nl;
+                }
+            }
+        }
+        for (int k = blockIdx.y * cw + threadIdx.x * 8; k < k_end; k += kThreads * 8) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (K <= kMaxSlots) {
+                // every slot's row load in flight before the first is summed; the
+                // sum still runs in ascending slot order
+                RowChunk<YT, F16> c[kMaxSlots];
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        float lo, hi;
-                        if constexpr (F16) {
-                            lo = f16_to_f32(static_cast<uint16_t>(v[d] & 0xFFFFu));
-                            hi = f16_to_f32(static_cast<uint16_t>(v[d] >> 16));
-                        } else {
-                            lo = __uint_as_float(v[d] << 16);
-                            hi = __uint_as_float(v[d] & 0xFFFF0000u);
-                        }
-                        acc[2 * d] = fmaf(w, lo, acc[2 * d]);
-                        acc[2 * d + 1] = fmaf(w, hi, acc[2 * d + 1]);
-                    }
-                } else {
-                    const floatx4 a = *reinterpret_cast<const floatx4*>(y + static_cast<int64_t>(r) * H + k);
-                    const floatx4 b = *reinterpret_cast<const floatx4*>(y + static_cast<int64_t>(r) * H + k + 4);
+                for (int i = 0; i < kMaxSlots; ++i)
+                    if (i < nl) c[i].load(y + static_cast<int64_t>(rows[i]) * H + k);
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        acc[d] = fmaf(w, a[d], acc[d]);
-                        acc[4 + d] = fmaf(w, b[d], acc[4 + d]);
-                    }
+                for (int i = 0; i < kMaxSlots; ++i)
+                    if (i < nl) c[i].accumulate(ws[i], acc);
+            } else {
+                for (int j = 0; j < K; ++j) {
+                    const int r = slot_row[static_cast<int64_t>(t) * K + j];
+                    if (r < 0) continue;
+                    RowChunk<YT, F16> c;
+                    c.load(y + static_cast<int64_t>(r) * H + k);
+                    c.accumulate(topk_w[static_cast<int64_t>(t) * K + j], acc);
                 }
             }
             float* o = out + static_cast<int64_t>(t) * H + k;

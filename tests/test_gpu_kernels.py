@@ -332,6 +332,9 @@ def _gemm_case(B, counts, H, I, seed=7):
                                         # 32-row groups in each 128-row half: 96 and 70 rows give 3, the
                                         # 200-row tile 4 and 3, 33 rows 2, and idle halves 0
                                         ([96, 200, 70, 33], 256, 128),
+                                        # full 256-row tiles (both halves with 4 groups) and 511 rows in two
+                                        # 256-row tiles; each half copies only its own active row blocks
+                                        ([256, 250, 511], 256, 128),
                                         # few rows per expert on average: the weight-streaming kernel, with
                                         # experts of 0, 1, 31, 33, 64, 65 and 150 rows (row groups of 64)
                                         ([150, 0, 1, 31, 33, 0, 0, 64, 65, 0, 0, 0, 0, 0, 0, 0] + [0] * 16,
