@@ -388,6 +388,29 @@ def test_grouped_gemm_exact_integers_many_tiles(B):
         assert np.array_equal(c2[r0:r1], h[r0:r1] @ wd[e]), f"down expert {e}"
 
 
+def test_grouped_gemm_exact_integers_max_experts(B):
+    """The largest local expert count the GEMMs take (1024): the tiled kernel's
+    per-expert tile table at its full size, with experts of 0 to 150 rows
+    (about 75 on average, so the tiled kernel runs); bit-exact on integer-grid
+    operands for both problems."""
+    counts = list(np.random.default_rng(21).integers(0, 151, size=1024))
+    s, offsets, a, wg, wu, wd = _gemm_case(B, counts, 256, 128, seed=22)
+    packed = B.moe_pack_weights(s, to_torch(_bf16(wg)), to_torch(_bf16(wu)), to_torch(_bf16(wd)))
+    off = to_torch(offsets)
+    c1 = B.moe_grouped_gemm(s, to_torch(_bf16(a)), off, packed, B.MOE_GEMM_GATE_UP, B.MOE_EPI_NONE,
+                            c_dtype=torch.float32)
+    h = (np.random.default_rng(23).integers(-4, 5, size=(s.cap, 128)) / 16).astype(np.float32)
+    c2 = B.moe_grouped_gemm(s, to_torch(h.astype(np.float16)), off, packed, B.MOE_GEMM_DOWN, B.MOE_EPI_NONE,
+                            c_dtype=torch.float32)
+    torch.cuda.synchronize()
+    c1, c2 = c1.cpu().numpy(), c2.cpu().numpy()
+    for e in range(len(counts)):
+        r0, r1 = offsets[e], offsets[e + 1]
+        gu = np.concatenate([a[r0:r1] @ wg[e], a[r0:r1] @ wu[e]], axis=1)
+        assert np.array_equal(c1[r0:r1], gu), f"gate/up expert {e}"
+        assert np.array_equal(c2[r0:r1], h[r0:r1] @ wd[e]), f"down expert {e}"
+
+
 def test_grouped_gemm_swiglu(B):
     """SwiGLU epilogue against float64: float32 output within accumulation-order
     noise; 16-bit outputs within half an ulp of their format (bf16: 2^-8
