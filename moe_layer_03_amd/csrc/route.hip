@@ -1237,6 +1237,7 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
     __shared__ uint8_t s_list[E];
     __shared__ int s_nu;
     __shared__ float s_nw[E];
+    __shared__ float s_bias[E];                            // the bias (0 without one), read from LDS below
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -1248,28 +1249,43 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
     const bool valid = t < T;
     const float Hu = static_cast<float>(H) * 0x1p-24f;
 
-    // squared norms of the router-weight columns (sum of the slice partials, once per workgroup)
+    // all slice partials of this lane's 8 experts are loaded before any is
+    // summed, and before the weight norms below: their latencies overlap.  The
+    // loads are unconditional (a lane past T or a slice past S reads token 0 or
+    // slice 0, then drops the value), so they issue back to back instead of
+    // one branch and one wait each.
+    float pv[SMAX][8];
+    float nxv[SMAX];
+    const int64_t tl_safe = valid ? t : 0;
+#pragma unroll
+    for (int sl = 0; sl < SMAX; ++sl) {
+        const bool live = valid && sl < S;
+        const int64_t row = static_cast<int64_t>(sl < S ? sl : 0) * T + tl_safe;
+        const float nv = nx[row];
+        nxv[sl] = live ? nv : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = part[row * E + s + 16 * i];
+            pv[sl][i] = live ? v : 0.0f;
+        }
+    }
+    // squared norms of the router-weight columns (sum of the slice partials, once
+    // per workgroup; loads unconditional, as above), and the bias
     for (int i = tid; i < E; i += NT) {
         s_flag[i] = 0;
+        float w2[SMAX];
+#pragma unroll
+        for (int sl = 0; sl < SMAX; ++sl) w2[sl] = nw[(sl < S ? sl : 0) * E + i];
         float n2 = 0.0f;
 #pragma unroll
         for (int sl = 0; sl < SMAX; ++sl)
-            if (sl < S) n2 += nw[sl * E + i];
+            if (sl < S) n2 += w2[sl];
         s_nw[i] = n2;
+        s_bias[i] = bias != nullptr ? bias[i] : 0.0f;
     }
     __syncthreads();
 
     // ---- screen: estimates, windows, theta, candidates ----
-    // all slice partials of this lane's 8 experts are loaded before any is summed
-    float pv[SMAX][8];
-    float nxv[SMAX];
-#pragma unroll
-    for (int sl = 0; sl < SMAX; ++sl) {
-        nxv[sl] = (valid && sl < S) ? nx[static_cast<int64_t>(sl) * T + t] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            pv[sl][i] = (valid && sl < S) ? part[(static_cast<int64_t>(sl) * T + t) * E + s + 16 * i] : 0.0f;
-    }
     float nxs = 0.0f;
 #pragma unroll
     for (int sl = 0; sl < SMAX; ++sl) nxs += nxv[sl];
@@ -1282,7 +1298,7 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
         float a = 0.0f;
 #pragma unroll
         for (int sl = 0; sl < SMAX; ++sl) a += pv[sl][i];
-        const float la = bias != nullptr ? a + bias[e] : a;
+        const float la = bias != nullptr ? a + s_bias[e] : a;
         const float d = 5.0f * Hu * (sx * sqrtf(s_nw[e])) + 0x1p-21f * fabsf(la) + 1e-30f;
         hi[i] = valid ? la + d : -INFINITY;
         klo[i] = make_key(valid ? la - d : -INFINITY, e);
@@ -1480,7 +1496,7 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
         if (valid && c < total) {
             const int e = s_chain[wave][base + c] & 0xFF;
             const float a = s_lg[base + c];
-            key[q] = make_key(bias != nullptr ? a + bias[e] : a, e);
+            key[q] = make_key(bias != nullptr ? a + s_bias[e] : a, e);
         } else {
             key[q] = 0ull;
         }
