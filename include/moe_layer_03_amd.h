@@ -100,14 +100,16 @@ size_t moe_route_workspace_bytes(const moe_shape* s);
  * path, and its stream has synchronised, ws holds at these byte offsets
  * (S = slices; slice s covers h in [s*H/S, (s+1)*H/S)):
  *   part_offset: float32 [S][T][E], the bf16-MFMA estimate of slice s of
- *                sum_h x[t,h] * w_router[h,e] (any summation order);
+ *                sum_h x[t,h] * w_router[h,e] (each 64-h chunk summed by MFMA
+ *                from zero, the chunk sums added in float32 in ascending h);
  *   nx_offset:   float32 [S][T], sum over slice s of x[t,h]^2;
  *   nw_offset:   float32 [S][E], sum over slice s of w_router[h,e]^2.
  * With u = 2^-24 and Hu = H*u, the router then forms, in float32 and in this
  * order:
  *   A[t,e] = ((part[0] + part[1]) + ...) + part[S-1], plus bias[e] if given;
  *   nX = sum_s nx[s][t], nW = sum_s nw[s][e] (ascending s);
- *   D[t,e] = 5 Hu (sqrt(nX) (1 + 3 Hu) sqrt(nW)) + 2^-21 |A| + 1e-30;
+ *   D[t,e] = ((1.0625 H + 192) u) (sqrt(nX) (1 + 3 Hu) sqrt(nW))
+ *            + 2^-21 |A| + 1e-30;
  * and its selection is exact because |A[t,e] - L[t,e]| <= D[t,e] for the
  * canonical logit L of moe_route().  Returns MOE_ERR_UNSUPPORTED when
  * (s, x_dtype, w_dtype) does not take the screened path.

@@ -887,14 +887,19 @@ void launch_route_dt(const moe_shape& s, const XT* x, const XT* w, const float* 
 //     gamma_H B_e + u |L_e|, gamma_H = H u / (1 - H u) (recursive summation).
 //   * One v_mfma adds 16 exact products to its accumulator.  Even an adder
 //     that aligned all 17 terms to the largest one without guard bits would
-//     err by at most 36 u times their absolute sum, so H/16 of them, plus at
-//     most 16 float32 additions of slice partials, stay within
-//     (2.25 H + 16) u B_e + u |A_e|.
+//     err by at most 36 u times their absolute sum.  Every 64-h chunk starts
+//     from a zero accumulator, so its four steps err by at most
+//     36 u (4 B_1 + 3 B_2 + 2 B_3 + B_4) (1 + 150 u) <= 144.1 u B_c over the
+//     chunk's products; the chunk sums, then the slice partials and the bias,
+//     are added in float32, one after another: at most H/64 + 1 additions,
+//     gamma_(H/64+1) times their absolute sum.  With the canonical chain's
+//     gamma_H this stays below (1.0625 H + 192) u B_e + 2 u |A_e| for
+//     H <= 65536 (gamma_n <= 1.004 n u there).
 //   * Cauchy-Schwarz: B_e <= ||x|| ||w_e||.  The norms come from float32 sums
 //     of squares, whose relative error (below 2 H u) is covered by the factor
 //     (1 + 3 H u).
-// Hence |A_e - L_e| <= D_e = 5 H u ||x|| ||w_e|| (1 + 3 H u) + 2^-21 |A_e| +
-// 1e-30, for H <= 65536.  If K experts f have A_f - D_f >= theta > A_e + D_e
+// Hence |A_e - L_e| <= D_e = (1.0625 H + 192) u ||x|| ||w_e|| (1 + 3 H u) +
+// 2^-21 |A_e| + 1e-30, for H <= 65536.  If K experts f have A_f - D_f >= theta > A_e + D_e
 // then L_f > L_e for each of them and e is outside the top K.  The
 // candidates are the experts with A_e + D_e >= theta, theta = the K-th
 // largest A_f - D_f: at least K of them (those defining theta), including
@@ -1022,7 +1027,14 @@ __global__ __launch_bounds__(256) void route_screen_kernel(
     const int kg = lane >> 5;             // which 8 of the 16 k of a step
     const int e = wave * 32 + col;        // this lane's expert (B operand)
 
+    // one chunk: its four k-steps accumulate from zero, and the chunk sum is
+    // then added to the running estimate in float32 (the bound counts on it)
     auto compute = [&](int st, int kc) {
+        floatx16 cacc[TM];
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) cacc[m][v] = 0.0f;
         const uint16_t* sx = s_ring[st];
         const uint16_t* sw = s_ring[st] + XSTAGE;
         const bool write_t = ((hbeg / kScrHC + kc) % nblk) == blk;   // this block stores this chunk of wT
@@ -1062,10 +1074,14 @@ __global__ __launch_bounds__(256) void route_screen_kernel(
                         nxp[m] = fmaf(hi, hi, nxp[m]);
                     }
                 }
-                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                 __builtin_bit_cast(bf16x8_t, b), acc[m], 0, 0, 0);
+                cacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                  __builtin_bit_cast(bf16x8_t, b), cacc[m], 0, 0, 0);
             }
         }
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[m][v] += cacc[m][v];
     };
 
     // ring: chunk kc lives in stage kc % NB; NB-1 chunks in flight (indices past
@@ -1290,6 +1306,7 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
 #pragma unroll
     for (int sl = 0; sl < SMAX; ++sl) nxs += nxv[sl];
     const float sx = sqrtf(nxs) * (1.0f + 3.0f * Hu);
+    const float dcoef = (1.0625f * static_cast<float>(H) + 192.0f) * 0x1p-24f;
     float hi[8];
     uint64_t klo[8];
 #pragma unroll
@@ -1299,7 +1316,7 @@ __global__ __launch_bounds__(WAVES * 64) void route_exact_kernel(
 #pragma unroll
         for (int sl = 0; sl < SMAX; ++sl) a += pv[sl][i];
         const float la = bias != nullptr ? a + s_bias[e] : a;
-        const float d = 5.0f * Hu * (sx * sqrtf(s_nw[e])) + 0x1p-21f * fabsf(la) + 1e-30f;
+        const float d = dcoef * (sx * sqrtf(s_nw[e])) + 0x1p-21f * fabsf(la) + 1e-30f;
         hi[i] = valid ? la + d : -INFINITY;
         klo[i] = make_key(valid ? la - d : -INFINITY, e);
     }

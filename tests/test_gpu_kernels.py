@@ -206,7 +206,8 @@ def _screen_bound(B, x, w, bias=None, K=8):
     f = np.float32
     Hu = f(H) * f(2.0 ** -24)
     sx = np.sqrt(nX) * (f(1.0) + f(3.0) * Hu)
-    D = (f(5.0) * Hu) * (sx[:, None] * np.sqrt(nW)[None, :]) + f(2.0 ** -21) * np.abs(A) + f(1e-30)
+    dcoef = (f(1.0625) * f(H) + f(192.0)) * f(2.0 ** -24)
+    D = dcoef * (sx[:, None] * np.sqrt(nW)[None, :]) + f(2.0 ** -21) * np.abs(A) + f(1e-30)
     assert A.dtype == np.float32 and D.dtype == np.float32
     L = oracle.router_logits(W.as_f32(x), W.as_f32(w), bias)
     gap = np.abs(A.astype(np.float64) - L.astype(np.float64))
