@@ -252,6 +252,16 @@ def test_route_screened_error_bound(B, kind):
     print(f"[{kind}] max |A - L| / D = {ratio:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("kind", ["scaled64", "cancelling"])
+@pytest.mark.parametrize("H", [128, 16384])
+def test_route_screened_error_bound_sizes(B, kind, H):
+    """The bound at the smallest reduction length the screened path takes (its constant term
+    dominates) and at four times the model's (its H term dominates; 16 H-slices)."""
+    x, w = _bound_inputs(kind, T=512, H=H, seed=13)
+    ratio = _screen_bound(B, x, w)
+    print(f"[{kind}, H={H}] max |A - L| / D = {ratio:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("name", ["prefill_ep4_shard", "skewed_prefill"])
 def test_route_screened_error_bound_workloads(B, name):
     """The same bound on the full prefill-shard inputs and on the skewed inputs (Zipf router bias)."""
